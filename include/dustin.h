@@ -1,0 +1,180 @@
+/*
+ * dustin.h — C ABI of the MI355X (gfx950) sparse-verification library.
+ *
+ * The three calls follow the middle steps of the verification workflow in the English
+ * Dustin summary ("Methodology" 3, steps 2-4):
+ *   dustin_srh_score          step 2: the importance map, computed from the semantic
+ *                             retrieval heads only ("Methodology" 1 and 2)
+ *   dustin_select             step 3: the fixed-size verification set I_verify
+ *                             ("Methodology" 1, last two sentences)
+ *   dustin_sparse_verify_attn step 4: the target verifies the draft block against the
+ *                             selected tokens only
+ *   dense_verify_attn         the full-cache verification it replaces ("Problem
+ *                             Statement": the target loads the full KV cache)
+ *
+ * Conventions for every call
+ *   - Pointers are DEVICE pointers unless marked (host).  bf16 data are raw 16-bit
+ *     patterns; every bf16 row (head_dim elements) is contiguous and 16-byte aligned.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream).  No call
+ *     allocates device memory, synchronises, or copies between host and device.
+ *   - Arguments are validated on the host before anything is enqueued; on error the
+ *     call returns a negative status and enqueues nothing (outputs untouched).
+ *   - Device-resident values (ctx_len, budget, idx, count, page tables, ...) cannot be
+ *     checked without a sync; kernels clamp each of them into range instead, so no
+ *     value can make a kernel read or write out of bounds.  Results for out-of-range
+ *     values are defined by that clamping, not by the method.
+ *   - The library keeps no state between calls.  Calls that share a workspace must be
+ *     ordered on one stream.
+ */
+#ifndef DUSTIN_H
+#define DUSTIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DUSTIN_OK = 0,
+    DUSTIN_ERR_INVALID_ARG = -1, /* null pointer, bad size, stride or alignment        */
+    DUSTIN_ERR_WORKSPACE = -2,   /* workspace missing or smaller than the size query  */
+    DUSTIN_ERR_UNSUPPORTED = -3, /* a shape outside what the kernels are built for    */
+    DUSTIN_ERR_HIP = -4          /* the HIP runtime reported an error at launch        */
+} dustin_status;
+
+/* Scoring modes of dustin_srh_score. */
+enum {
+    /* Sum over every (SRH query head, query) pair of the softmax probability of the
+       token under that pair (English Dustin summary, "Methodology" 1: attention scores
+       of the target-historical and draft-lookahead queries form the importance map). */
+    DUSTIN_SCORE_PROB_SUM = 0,
+    /* Sum over the SRH query heads and over the queries {0, n_q-1} of the scaled
+       pre-softmax logit (German Vegas summary, 2A formula restricted to the first and
+       the bonus query of 2B, "Collect-2-Query").  Query 0 counts once when n_q == 1.  */
+    DUSTIN_SCORE_LOGIT_SUM2 = 1
+};
+
+/* A bf16 K or V cache of one layer, contiguous or paged.
+ *   contiguous: row(b, t, h) = base + b*stride_batch + t*stride_token + h*stride_head
+ *               for 0 <= t < n_tokens
+ *   paged     : row(b, t, h) = base + page_table[b*max_pages + t/page_size]*stride_page
+ *                                   + (t % page_size)*stride_token + h*stride_head
+ *               for 0 <= t < max_pages*page_size; page ids are clamped to [0, num_pages)
+ * Strides are in elements, multiples of 8 (16-byte rows).  The gamma+1 tokens being
+ * verified must already be stored at positions ctx_len[b] .. ctx_len[b]+gamma. */
+typedef struct {
+    const void *base;
+    int64_t stride_batch;        /* unused when paged                                  */
+    int64_t stride_token;
+    int64_t stride_head;
+    int32_t n_tokens;            /* contiguous: tokens addressable per sequence        */
+    int32_t n_heads;             /* KV heads stored in the view                        */
+    const int32_t *page_table;   /* NULL = contiguous; else [B][max_pages] (device)    */
+    int64_t stride_page;
+    int32_t page_size;           /* power of two                                       */
+    int32_t max_pages;
+    int32_t num_pages;
+} dustin_kv_view;
+
+/* One scored stream: the K cache of one model layer, one of its KV heads, and the
+ * number of SRH query heads that read that KV head. */
+typedef struct {
+    dustin_kv_view k;
+    int32_t kv_head;
+    int32_t n_qheads;
+} dustin_srh_group;
+
+const char *dustin_status_string(dustin_status s);
+
+/* ---------------------------------------------------------------------------------
+ * Step 2 — SRH importance scoring.
+ * For every sequence b and token i < ctx_len[b] (clamped to [0, n_max] and to each
+ * view's capacity):
+ *   PROB_SUM   score[b][i] = sum over groups g, query heads h of g, queries j < n_q of
+ *                            softmax_i(scale * q[b][h][j] . K_g[b][i])
+ *   LOGIT_SUM2 score[b][i] = sum over groups, heads, j in {0, n_q-1} of
+ *                            scale * q[b][h][j] . K_g[b][i]
+ * score[b][i] = 0 for ctx_len[b] <= i < n_max.  One call scores one signal (the draft
+ * lookahead queries, or the target-historical queries); the softmax runs over the
+ * committed context [0, ctx_len[b]).
+ *   groups : (host) [n_groups], 1 <= n_groups <= 16; all groups share head_dim
+ *   q      : bf16 [B][sum of n_qheads][n_q][head_dim], heads in group order
+ *   head_dim in {64, 128}; 1 <= n_q <= 16; pairs per group (n_qheads * queries used)
+ *   at most 64
+ *   score  : fp32 [B][n_max], fully written
+ *   workspace: at least dustin_srh_score_workspace_size(...) bytes, any contents
+ * ------------------------------------------------------------------------------- */
+dustin_status dustin_srh_score_workspace_size(int B, int n_max, int total_qheads, int n_q,
+                                              int mode, size_t *bytes /* host */);
+dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_groups,
+                               const dustin_srh_group *groups /* host */, int head_dim,
+                               const void *q, int n_q, float scale, int mode, float *score,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Step 3 — hybrid budgeted selection of I_verify.
+ * Per sequence b, with N = ctx_len[b] clamped to [0, n_max] and
+ * k = min(budget[b], N, k_max):
+ *   k == N : I = [0, N)
+ *   else   : s = min(n_sink[b], k); w = min(n_window[b], k - s)
+ *            P = [0, s) u [N - w, N)                     (always kept)
+ *            m' = min(m[b], k - |P|)                     (0 when score_draft is NULL)
+ *            D = the m' best tokens of [0,N) \ P by score_draft
+ *            T = the k - |P| - m' best tokens of [0,N) \ (P u D) by score_target
+ *            I = P u D u T
+ *   "best": larger score first, then smaller position; -0 equals +0.  NaN scores are
+ *   outside the contract.
+ *   idx   : int32 [B][k_max] ascending positions, entries count[b].. set to -1
+ *   count : int32 [B] = |I|
+ *   budget, n_sink, n_window, m : int32 [B] (negative values act as 0)
+ *   n_max <= 131072.  workspace: dustin_select_workspace_size(...) bytes (may be 0).
+ * ------------------------------------------------------------------------------- */
+dustin_status dustin_select_workspace_size(int B, int n_max, size_t *bytes /* host */);
+dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const float *score_draft,
+                            const float *score_target, const int32_t *budget,
+                            const int32_t *n_sink, const int32_t *n_window, const int32_t *m,
+                            int k_max, int32_t *idx, int32_t *count, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Step 4 — verification attention over the selected tokens.
+ * For sequence b, verify query t (0 <= t < n_verify) and query head h (KV head
+ * g = h / (Hq/Hkv)), the attended set is I_b u {ctx_len[b] + j : 0 <= j <= t} with
+ * I_b = idx[b][0 .. count[b]) (count clamped to [0, k_max], positions clamped to
+ * [0, ctx_len[b])):
+ *   out[b][t][h] = sum_x softmax_x(scale * q[b][t][h] . K[b][x][g]) V[b][x][g]
+ *   lse[b][h][t] = ln sum_x exp(scale * q[b][t][h] . K[b][x][g])
+ *   q, out : bf16 [B][n_verify][Hq][head_dim];  lse : fp32 [B][Hq][n_verify]
+ *   head_dim in {64, 128}; 1 <= n_verify <= 16; Hq % Hkv == 0
+ *   workspace: dustin_sparse_verify_attn_workspace_size(...) bytes.  It holds split
+ *   partials and per-(sequence, KV head) counters: it must be zero-filled before its
+ *   first use and must not be written by anything else between calls (every call
+ *   leaves the counters at zero).
+ * dense_verify_attn is the same with I_b = [0, ctx_len[b]); n_max bounds ctx_len.
+ * ------------------------------------------------------------------------------- */
+dustin_status dustin_sparse_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_dim,
+                                                       int n_verify, int k_max,
+                                                       size_t *bytes /* host */);
+dustin_status dustin_sparse_verify_attn(int B, int Hq, int Hkv, int head_dim, int n_verify,
+                                        const void *q, const dustin_kv_view *k /* host */,
+                                        const dustin_kv_view *v /* host */,
+                                        const int32_t *ctx_len, const int32_t *idx,
+                                        const int32_t *count, int k_max, float scale,
+                                        void *out, float *lse, void *workspace,
+                                        size_t workspace_bytes, void *stream);
+
+dustin_status dense_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_dim,
+                                               int n_verify, int n_max,
+                                               size_t *bytes /* host */);
+dustin_status dense_verify_attn(int B, int Hq, int Hkv, int head_dim, int n_verify,
+                                const void *q, const dustin_kv_view *k /* host */,
+                                const dustin_kv_view *v /* host */, const int32_t *ctx_len,
+                                int n_max, float scale, void *out, float *lse,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DUSTIN_H */

@@ -113,9 +113,6 @@ int oracle_select(int B, int n_max, const int32_t *ctx_len,
     if (B < 0 || n_max < 0 || k_max < 0 || !ctx_len || !score_target || !budget || !n_sink ||
         !n_window || !m || !idx || !count)
         return -1;
-    for (int b = 0; b < B; ++b)
-        if (m[b] > 0 && !score_draft)
-            return -1;
     cand *c = (cand *)malloc(sizeof(cand) * (size_t)(n_max > 0 ? n_max : 1));
     unsigned char *in = (unsigned char *)malloc((size_t)(n_max > 0 ? n_max : 1));
     if (!c || !in) {
@@ -140,7 +137,7 @@ int oracle_select(int B, int n_max, const int32_t *ctx_len,
             for (int i = N - w; i < N; ++i)
                 in[i] = 1;
             int p = s + w;
-            int md = clampi(m[b], 0, k - p);
+            int md = score_draft ? clampi(m[b], 0, k - p) : 0; /* no draft signal: no draft tier */
             int r = k - p - md;
             /* tier 1: top-md by the draft score among the unprotected tokens */
             if (md > 0) {

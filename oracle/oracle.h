@@ -42,7 +42,7 @@ int oracle_score_stream(int B, int n_rows, int n_max, const int32_t *ctx_len, in
                         double scale, int mode, double *acc);
 
 /* Hybrid budgeted selection of I_verify for every sequence.
- *   score_draft / score_target : [B][n_max]; score_draft may be NULL iff every m[b] == 0
+ *   score_draft / score_target : [B][n_max]; score_draft NULL = no draft tier (m' = 0)
  *   budget, n_sink, n_window, m : [B]
  *   idx   : [B][k_max] out, ascending positions, tail filled with -1
  *   count : [B] out, = min(budget[b], ctx_len[b], k_max)                             */

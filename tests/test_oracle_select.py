@@ -154,3 +154,11 @@ def test_ragged_batch():
     for b in range(B):
         one, _, c1 = sel1(int(ctx[b]), int(bud[b]), 4, 8, 10, sd[b, :ctx[b]], st[b, :ctx[b]], k_max=k_max)
         assert list(idx[b, :cnt[b]]) == one and cnt[b] == c1 == min(ctx[b], bud[b])
+
+
+def test_no_draft_signal_means_no_draft_tier():
+    rng = np.random.default_rng(12)
+    N, t = 100, rng.standard_normal(100)
+    a, _, _ = sel1(N, 20, 2, 4, 7, None, t)
+    b, _, _ = sel1(N, 20, 2, 4, 0, np.zeros(N), t)
+    assert a == b
