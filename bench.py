@@ -1,0 +1,232 @@
+"""Benchmark of one sparse-verification step on one MI355X.
+
+Workload: Qwen2.5-72B-shaped target (80 layers, 64 query heads, 8 KV heads, head dim
+128, bf16), batch 8, 32768-token contexts, gamma = 4 (5 verify queries), budget 2048
+(16 sinks, 256 window, m = 768), 4 draft + 4 target SRH streams.  All inputs are seeded
+synthetic tensors resident in HBM before timing starts; every layer has its own K/V
+buffers (86 GB in total), so no layer's gathered rows are served from the last-level
+cache by an earlier layer.
+
+One step = draft-SRH scoring + target-SRH scoring + selection + sparse verification
+attention over all 80 layers.  `value` is the step's algorithmic HBM bytes divided by
+the step time (GB/s); the step time itself is `step_us`.  The roofline entry is for the
+dominant kernel (verification attention): its algorithmic bytes per launch divided by
+its average launch duration, timed with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-verify step µs + achieved HBM GB/s (B=8, 32k ctx, budget 2048, γ=4)"
+HBM_PEAK_GBS = 8000.0
+
+
+def attn_bytes(B, Hq, Hkv, d, nv, counts):
+    """Algorithmic bytes of one verification-attention launch: the gathered K and V rows
+    of the selected tokens and of the new block, Q, O, LSE and the index list."""
+    rows = sum(int(c) + nv for c in counts)
+    return rows * Hkv * d * 2 * 2 + 2 * B * nv * Hq * d * 2 + B * Hq * nv * 4 + sum(int(c) for c in counts) * 4
+
+
+def score_bytes(B, n_ctx, streams_d, n_out):
+    """Algorithmic bytes of scoring: every scored K row once, and the score vectors."""
+    return sum(B * n_ctx * d * 2 for d in streams_d) + n_out * B * n_ctx * 4
+
+
+def select_bytes(B, n_ctx, k):
+    return 2 * B * n_ctx * 4 + B * k * 4 + B * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=80, help="target layers (80 = the whole 72B-shaped model)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
+    ap.add_argument("--dense-layers", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the sparse-verification path here is a single-GPU build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_kv_attention_amd import workloads as W
+    from sparse_kv_attention_amd.pipeline import SparseVerifyStep
+
+    dev = torch.device("cuda:0")
+    w = W.QWEN72B
+    if args.layers != w.target.layers:
+        w = W.shrink(w, target=W.ModelShape(args.layers, w.target.hq, w.target.hkv, w.target.d),
+                     srh_target=tuple((l % args.layers, h) for l, h in w.srh_target))
+    t0 = time.time()
+    inp = W.make_inputs(w, device=dev)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t0:.1f}s: {len(inp.k_cache)} layers", file=sys.stderr, flush=True)
+    step = SparseVerifyStep(inp)
+    T = w.target
+    B, nv = w.batch, w.n_verify
+    stream = torch.cuda.current_stream()
+
+    # ---- warmup ----
+    for _ in range(args.warmup):
+        step.step()
+    torch.cuda.synchronize()
+    counts = step.count.cpu().tolist()
+
+    # ---- timed steps ----
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step.step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    step_ms = e0.elapsed_time(e1) / args.steps
+
+    # ---- per-stage and per-launch timing (separate loops, same stream) ----
+    def timed(fn, reps):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    reps = max(5, args.steps // 2)
+    us_score = timed(step.score, reps)
+    us_select = timed(step.select, reps)
+    attn_layers = step.layers
+    # every attention launch bracketed by its own events on the launch stream
+    durs = []
+    for _ in range(reps):
+        evs = [(ev(), ev()) for _ in attn_layers]
+        for (a, b), l in zip(evs, attn_layers):
+            a.record(stream)
+            step.attn(l)
+            b.record(stream)
+        torch.cuda.synchronize()
+        durs += [a.elapsed_time(b) * 1e3 for a, b in evs]
+    us_attn_launch = float(np.mean(durs))
+    us_attn_all = timed(lambda: [step.attn(l) for l in attn_layers], reps)
+    dl = attn_layers[: max(1, min(args.dense_layers, len(attn_layers)))]
+    us_dense_layer = timed(lambda: [step.dense(l) for l in dl], 3) / len(dl)
+
+    # ---- bytes ----
+    n_ctx = inp.n_max
+    b_attn = attn_bytes(B, T.hq, T.hkv, T.d, nv, counts)
+    d_streams = [w.draft.d] * len(inp.draft_groups) + [T.d] * len(inp.target_groups)
+    b_score = score_bytes(B, n_ctx, d_streams, 2)
+    b_select = select_bytes(B, n_ctx, inp.k_max)
+    b_step = b_score + b_select + len(attn_layers) * b_attn
+    b_dense = attn_bytes(B, T.hq, T.hkv, T.d, nv, [n_ctx] * B) - B * n_ctx * 4   # no index list
+    gbs = b_step / (step_ms * 1e-3) / 1e9
+    attn_gbs = b_attn / (us_attn_launch * 1e-6) / 1e9
+
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/Q, 1% needle keys at cosine 0.5 in the SRH streams)",
+        "config": {"workload": w.name, "batch": B, "ctx": n_ctx, "budget": w.budget, "gamma": w.gamma,
+                   "n_sink": w.n_sink, "n_window": w.n_window, "m": w.m, "layers": len(attn_layers),
+                   "hq": T.hq, "hkv": T.hkv, "head_dim": T.d,
+                   "srh_streams": {"draft": len(inp.draft_groups), "target": len(inp.target_groups)}},
+        "step_us": round(step_ms * 1e3, 1),
+        "stages_us": {"score_both_signals": round(us_score, 2), "select": round(us_select, 2),
+                      "attn_per_launch": round(us_attn_launch, 2), "attn_all_layers": round(us_attn_all, 1)},
+        "bytes": {"step": b_step, "attn_per_launch": b_attn, "score": b_score, "select": b_select},
+        "score_gbs": round(b_score / (us_score * 1e-6) / 1e9, 1),
+        "dense_attn_per_layer_us": round(us_dense_layer, 2),
+        "dense_attn_gbs": round(b_dense / (us_dense_layer * 1e-6) / 1e9, 1),
+        "attn_speedup_vs_dense": round(us_dense_layer / us_attn_launch, 2),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "verify_attn_kernel<128,3> (sparse verification attention, one layer)"},
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, step, args.cpu_seconds, b_attn, b_score, b_select, attn_layers)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inp, step, budget_s, b_attn, b_score, b_select, layers):
+    """The oracle (single-threaded C, fp64) on a bounded sample of the same workload:
+    sequence 0's scoring (both signals), selection and as many layers of its sparse
+    attention as fit the time budget.  Reported as algorithmic GB/s of that sample."""
+    import numpy as np
+    import torch
+
+    from oracle import oracle as O
+
+    u16 = lambda t: t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+    w = inp.w
+    B = w.batch
+    n = inp.n_max
+    ctx = inp.ctx_len.cpu().numpy()[:1]
+    secs = 0.0
+    for groups, q, caches, d in ((inp.draft_groups, inp.q_srh_draft, inp.draft_k, w.draft.d),
+                                 (inp.target_groups, inp.q_srh_target, inp.k_cache, w.target.d)):
+        acc = np.zeros((1, n))
+        qo = 0
+        for g in groups:
+            K = u16(caches[g.layer][:1, :n, g.kv_head])
+            Q = u16(q[:1, qo:qo + len(g.qheads)])
+            t = time.perf_counter()
+            O.score_stream(K, Q, ctx, n, 1.0 / math.sqrt(d), O.PROB_SUM, acc)
+            secs += time.perf_counter() - t
+            qo += len(g.qheads)
+    sd = step.score_draft[:1].double().cpu().numpy()
+    st = step.score_target[:1].double().cpu().numpy()
+    c = lambda x: x.cpu().numpy()[:1]
+    t = time.perf_counter()
+    idx, cnt = O.select(ctx, sd, st, c(inp.budget), c(inp.n_sink), c(inp.n_window), c(inp.m), inp.k_max)
+    secs += time.perf_counter() - t
+    nbytes = (b_score + b_select) / B
+    n_layers = 0
+    for l in layers:
+        rows = int(ctx[0]) + w.n_verify
+        K = u16(inp.k_cache[l][:1, :rows])
+        V = u16(inp.v_cache[l][:1, :rows])
+        Q = u16(inp.q_verify[l][:1])
+        t = time.perf_counter()
+        O.verify_attn(Q, K, V, ctx, idx, cnt, 1.0 / math.sqrt(w.target.d), w.target.hkv)
+        secs += time.perf_counter() - t
+        nbytes += b_attn / B
+        n_layers += 1
+        if secs >= budget_s:
+            break
+    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"sequence 0 of 8: SRH scoring (both signals), selection, sparse attention over "
+                      f"{n_layers} of {len(layers)} layers; {secs:.1f} s of oracle time",
+            "seconds": round(secs, 2), "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -129,7 +129,7 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
  *   idx   : int32 [B][k_max] ascending positions, entries count[b].. set to -1
  *   count : int32 [B] = |I|
  *   budget, n_sink, n_window, m : int32 [B] (negative values act as 0)
- *   n_max <= 131072.  workspace: dustin_select_workspace_size(...) bytes (may be 0).
+ *   n_max <= 65536.  workspace: dustin_select_workspace_size(...) bytes (may be 0).
  * ------------------------------------------------------------------------------- */
 dustin_status dustin_select_workspace_size(int B, int n_max, size_t *bytes /* host */);
 dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const float *score_draft,

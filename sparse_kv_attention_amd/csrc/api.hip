@@ -1,0 +1,352 @@
+// C-ABI entry points: host-side validation, workspace layout and kernel launches.
+// Nothing here touches device memory or synchronises; every check uses host values only.
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "dustin.h"
+#include "launch.hpp"
+
+using namespace dustin;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// A view is usable for `heads` KV heads and at least `min_tokens` tokens per sequence.
+bool view_ok(const dustin_kv_view *v, int heads, int min_tokens)
+{
+    if (!v || !v->base || !aligned16(v->base))
+        return false;
+    if (v->stride_token <= 0 || v->stride_head < 0 || v->stride_batch < 0 || v->n_heads < heads)
+        return false;
+    if ((v->stride_token | v->stride_head | v->stride_batch | v->stride_page) & 7)
+        return false;
+    if (v->page_table) {
+        if (v->page_size <= 0 || (v->page_size & (v->page_size - 1)) || v->max_pages <= 0 ||
+            v->num_pages <= 0 || v->stride_page <= 0)
+            return false;
+        if ((int64_t)v->max_pages * v->page_size > (1ll << 30))
+            return false;
+        return v->max_pages * v->page_size >= min_tokens;
+    }
+    return v->n_tokens >= min_tokens && v->n_tokens > 0;
+}
+
+int view_cap(const dustin_kv_view *v)
+{
+    return v->page_table ? v->max_pages * v->page_size : v->n_tokens;
+}
+
+int env_int(const char *name, int dflt)
+{
+    const char *s = getenv(name);
+    if (!s || !*s)
+        return dflt;
+    const int v = atoi(s);
+    return v > 0 ? v : dflt;
+}
+
+// Target number of attention workgroups per launch (about 2 resident per CU on 256 CUs,
+// more for long lists so the tail of the grid balances).
+int attn_target_wgs(int max_list)
+{
+    const int dflt = max_list > 8192 ? 2048 : 512;
+    return env_int("DUSTIN_ATTN_TARGET_WGS", dflt);
+}
+
+struct AttnWs {
+    AttnPlan plan;
+    size_t counters_off, part_off, bytes;
+};
+
+AttnWs attn_workspace(int B, int Hq, int Hkv, int n_verify, int max_list)
+{
+    AttnWs w;
+    const int G = Hq / Hkv;
+    w.plan = plan_attn(B, Hkv, G, n_verify, max_list, attn_target_wgs(max_list));
+    w.counters_off = 0;
+    w.part_off = align_up(sizeof(int) * (size_t)w.plan.pairs);
+    w.bytes = w.part_off + align_up(sizeof(float) * w.plan.part_floats);
+    return w;
+}
+
+bool attn_shape_ok(int B, int Hq, int Hkv, int head_dim, int n_verify, dustin_status &st)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || n_verify <= 0) {
+        st = DUSTIN_ERR_INVALID_ARG;
+        return false;
+    }
+    if (Hq % Hkv) {
+        st = DUSTIN_ERR_INVALID_ARG;
+        return false;
+    }
+    if ((head_dim != 64 && head_dim != 128) || n_verify > 16 || Hq / Hkv * n_verify > 1024) {
+        st = DUSTIN_ERR_UNSUPPORTED;
+        return false;
+    }
+    return true;
+}
+
+dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const void *q,
+                       const dustin_kv_view *k, const dustin_kv_view *v, const int32_t *ctx_len,
+                       const int32_t *idx, const int32_t *count, int k_max, int n_max,
+                       float scale, void *out, float *lse, void *ws, size_t ws_bytes, void *stream)
+{
+    dustin_status st = DUSTIN_OK;
+    if (!attn_shape_ok(B, Hq, Hkv, head_dim, n_verify, st))
+        return st;
+    if (B == 0)
+        return DUSTIN_OK;
+    const bool sparse = idx != nullptr || count != nullptr;
+    if (!q || !ctx_len || !out || !lse || !aligned16(q) || !aligned16(out))
+        return DUSTIN_ERR_INVALID_ARG;
+    if (sparse && (!idx || !count || k_max < 0))
+        return DUSTIN_ERR_INVALID_ARG;
+    if (n_max < 0 || !(scale == scale))
+        return DUSTIN_ERR_INVALID_ARG;
+    if (!view_ok(k, Hkv, n_verify) || !view_ok(v, Hkv, n_verify))
+        return DUSTIN_ERR_INVALID_ARG;
+    const int cap = std::min(view_cap(k), view_cap(v));
+    const int ctx_clamp = std::min(cap - n_verify, sparse ? cap - n_verify : n_max);
+    // the split plan depends on host sizes only, exactly as in the workspace-size queries
+    const int max_list = (sparse ? k_max : n_max) + n_verify;
+    const AttnWs lay = attn_workspace(B, Hq, Hkv, n_verify, max_list);
+    if (lay.bytes > 0 && (!ws || ws_bytes < lay.bytes || !aligned16(ws)))
+        return DUSTIN_ERR_WORKSPACE;
+
+    AttnArgs a;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.G = Hq / Hkv;
+    a.nv = n_verify;
+    a.GV = a.G * n_verify;
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = make_view(*k);
+    a.v = make_view(*v);
+    a.ctx_len = ctx_len;
+    a.idx = sparse ? idx : nullptr;
+    a.count = sparse ? count : nullptr;
+    a.k_max = sparse ? k_max : 0;
+    a.ctx_clamp = ctx_clamp;
+    a.scale_log2 = scale * kLog2e;
+    a.out = static_cast<uint16_t *>(out);
+    a.lse = lse;
+    a.counters = reinterpret_cast<int *>(static_cast<char *>(ws) + lay.counters_off);
+    a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.part_off);
+    a.splits = lay.plan.splits;
+    a.cps = lay.plan.cps;
+    a.qgroups = lay.plan.qgroups;
+    a.pairs = lay.plan.pairs;
+    const hipError_t e = launch_attn(a, head_dim, lay.plan.qt, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
+}
+
+struct ScoreWs {
+    int n_pad, n_tiles, total_pairs;
+    size_t logits_off, max_off, sum_off, bytes;
+};
+
+int pairs_per_qhead(int n_q, int mode) { return mode == DUSTIN_SCORE_PROB_SUM ? n_q : std::min(2, n_q); }
+
+ScoreWs score_workspace(int B, int n_max, int total_qheads, int n_q, int mode)
+{
+    ScoreWs w;
+    w.n_pad = (n_max + 3) / 4 * 4;
+    w.n_tiles = std::max(1, (n_max + kProbTile - 1) / kProbTile);
+    w.total_pairs = total_qheads * pairs_per_qhead(n_q, mode);
+    const size_t stats = mode == DUSTIN_SCORE_PROB_SUM ? (size_t)B * w.total_pairs * w.n_tiles : 0;
+    w.logits_off = 0;
+    w.max_off = align_up(sizeof(float) * (size_t)B * w.total_pairs * w.n_pad);
+    w.sum_off = w.max_off + align_up(sizeof(double) * stats);
+    w.bytes = w.sum_off + align_up(sizeof(float) * stats);
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dustin_status_string(dustin_status s)
+{
+    switch (s) {
+    case DUSTIN_OK: return "ok";
+    case DUSTIN_ERR_INVALID_ARG: return "invalid argument";
+    case DUSTIN_ERR_WORKSPACE: return "workspace missing or too small";
+    case DUSTIN_ERR_UNSUPPORTED: return "unsupported shape";
+    case DUSTIN_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+dustin_status dustin_srh_score_workspace_size(int B, int n_max, int total_qheads, int n_q, int mode,
+                                              size_t *bytes)
+{
+    if (!bytes || B < 0 || n_max < 0 || total_qheads < 0 || n_q <= 0 || n_q > 16 ||
+        (mode != DUSTIN_SCORE_PROB_SUM && mode != DUSTIN_SCORE_LOGIT_SUM2))
+        return DUSTIN_ERR_INVALID_ARG;
+    *bytes = score_workspace(B, n_max, total_qheads, n_q, mode).bytes;
+    return DUSTIN_OK;
+}
+
+dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_groups,
+                               const dustin_srh_group *groups, int head_dim, const void *q, int n_q,
+                               float scale, int mode, float *score, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    if (B < 0 || n_max < 0 || n_q <= 0 || !(scale == scale))
+        return DUSTIN_ERR_INVALID_ARG;
+    if (mode != DUSTIN_SCORE_PROB_SUM && mode != DUSTIN_SCORE_LOGIT_SUM2)
+        return DUSTIN_ERR_INVALID_ARG;
+    if (n_groups < 1 || !groups)
+        return DUSTIN_ERR_INVALID_ARG;
+    if (n_groups > kMaxGroups || (head_dim != 64 && head_dim != 128) || n_q > 16)
+        return DUSTIN_ERR_UNSUPPORTED;
+    if (B == 0 || n_max == 0)
+        return DUSTIN_OK;
+    if (!ctx_len || !q || !score || !aligned16(q))
+        return DUSTIN_ERR_INVALID_ARG;
+    const int ppq = pairs_per_qhead(n_q, mode);
+    int total_qheads = 0, max_pairs = 0, ctx_clamp = n_max;
+    for (int i = 0; i < n_groups; ++i) {
+        const dustin_srh_group &g = groups[i];
+        if (g.n_qheads <= 0 || g.kv_head < 0 || !view_ok(&g.k, g.kv_head + 1, 1))
+            return DUSTIN_ERR_INVALID_ARG;
+        if (g.n_qheads * ppq > kMaxPairsPerGroup)
+            return DUSTIN_ERR_UNSUPPORTED;
+        total_qheads += g.n_qheads;
+        max_pairs = std::max(max_pairs, g.n_qheads * ppq);
+        ctx_clamp = std::min(ctx_clamp, view_cap(&g.k));
+    }
+    const ScoreWs lay = score_workspace(B, n_max, total_qheads, n_q, mode);
+    if (!workspace || workspace_bytes < lay.bytes || !aligned16(workspace))
+        return DUSTIN_ERR_WORKSPACE;
+
+    ScoreArgs a;
+    a.B = B;
+    a.n_max = n_max;
+    a.n_pad = lay.n_pad;
+    a.n_groups = n_groups;
+    a.n_q = n_q;
+    a.mode = mode;
+    a.total_qheads = total_qheads;
+    a.total_pairs = lay.total_pairs;
+    a.n_tiles = lay.n_tiles;
+    a.ctx_clamp = ctx_clamp;
+    a.ctx_len = ctx_len;
+    a.q = static_cast<const uint16_t *>(q);
+    a.mul = mode == DUSTIN_SCORE_PROB_SUM ? (double)scale * 1.4426950408889634 : (double)scale;
+    a.logits = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.logits_off);
+    a.tile_max = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.max_off);
+    a.tile_sum = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.sum_off);
+    a.score = score;
+    int qh = 0, pr = 0;
+    for (int i = 0; i < n_groups; ++i) {
+        ScoreGroup &sg = a.grp[i];
+        sg.k = make_view(groups[i].k);
+        sg.kv_head = groups[i].kv_head;
+        sg.q_head0 = qh;
+        sg.n_qheads = groups[i].n_qheads;
+        sg.pair0 = pr;
+        sg.n_pairs = groups[i].n_qheads * ppq;
+        qh += sg.n_qheads;
+        pr += sg.n_pairs;
+    }
+    const hipError_t e = launch_score(a, head_dim, max_pairs, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
+}
+
+dustin_status dustin_select_workspace_size(int B, int n_max, size_t *bytes)
+{
+    if (!bytes || B < 0 || n_max < 0)
+        return DUSTIN_ERR_INVALID_ARG;
+    *bytes = 0;
+    return DUSTIN_OK;
+}
+
+dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const float *score_draft,
+                            const float *score_target, const int32_t *budget,
+                            const int32_t *n_sink, const int32_t *n_window, const int32_t *m,
+                            int k_max, int32_t *idx, int32_t *count, void *workspace,
+                            size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    if (B < 0 || n_max < 0 || k_max < 0)
+        return DUSTIN_ERR_INVALID_ARG;
+    if (n_max > kSelectMaxN)
+        return DUSTIN_ERR_UNSUPPORTED;
+    if (B == 0)
+        return DUSTIN_OK;
+    if (!ctx_len || !score_target || !budget || !n_sink || !n_window || !m || !count ||
+        (k_max > 0 && !idx))
+        return DUSTIN_ERR_INVALID_ARG;
+    SelectArgs a;
+    a.B = B;
+    a.n_max = n_max;
+    a.k_max = k_max;
+    a.ctx_len = ctx_len;
+    a.score_draft = score_draft;
+    a.score_target = score_target;
+    a.budget = budget;
+    a.n_sink = n_sink;
+    a.n_window = n_window;
+    a.m = m;
+    a.idx = idx;
+    a.count = count;
+    const hipError_t e = launch_select(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
+}
+
+dustin_status dustin_sparse_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_dim,
+                                                       int n_verify, int k_max, size_t *bytes)
+{
+    dustin_status st = DUSTIN_OK;
+    if (!bytes || k_max < 0)
+        return DUSTIN_ERR_INVALID_ARG;
+    if (!attn_shape_ok(B, Hq, Hkv, head_dim, n_verify, st))
+        return st;
+    *bytes = attn_workspace(B, Hq, Hkv, n_verify, k_max + n_verify).bytes;
+    return DUSTIN_OK;
+}
+
+dustin_status dustin_sparse_verify_attn(int B, int Hq, int Hkv, int head_dim, int n_verify,
+                                        const void *q, const dustin_kv_view *k,
+                                        const dustin_kv_view *v, const int32_t *ctx_len,
+                                        const int32_t *idx, const int32_t *count, int k_max,
+                                        float scale, void *out, float *lse, void *workspace,
+                                        size_t workspace_bytes, void *stream)
+{
+    if (!idx || !count)
+        return DUSTIN_ERR_INVALID_ARG;
+    return run_attn(B, Hq, Hkv, head_dim, n_verify, q, k, v, ctx_len, idx, count, k_max, 0, scale,
+                    out, lse, workspace, workspace_bytes, stream);
+}
+
+dustin_status dense_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_dim, int n_verify,
+                                               int n_max, size_t *bytes)
+{
+    dustin_status st = DUSTIN_OK;
+    if (!bytes || n_max < 0)
+        return DUSTIN_ERR_INVALID_ARG;
+    if (!attn_shape_ok(B, Hq, Hkv, head_dim, n_verify, st))
+        return st;
+    *bytes = attn_workspace(B, Hq, Hkv, n_verify, n_max + n_verify).bytes;
+    return DUSTIN_OK;
+}
+
+dustin_status dense_verify_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const void *q,
+                                const dustin_kv_view *k, const dustin_kv_view *v,
+                                const int32_t *ctx_len, int n_max, float scale, void *out,
+                                float *lse, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return run_attn(B, Hq, Hkv, head_dim, n_verify, q, k, v, ctx_len, nullptr, nullptr, 0, n_max,
+                    scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

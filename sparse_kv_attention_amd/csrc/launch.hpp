@@ -1,0 +1,84 @@
+// Kernel launch interface between the C-ABI entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace dustin {
+
+// ---------------------------------------------------------------- attention
+constexpr int kMaxQT = 5;   // 16-row query tiles held by one workgroup
+
+struct AttnArgs {
+    int B, Hq, Hkv, G, nv, GV;
+    const uint16_t *q;
+    KvView k, v;
+    const int32_t *ctx_len;
+    const int32_t *idx;      // nullptr = dense: the list is [0, ctx_len[b])
+    const int32_t *count;
+    int k_max;
+    int ctx_clamp;           // ctx_len is clamped to [0, ctx_clamp]
+    float scale_log2;        // softmax scale * log2(e)
+    uint16_t *out;
+    float *lse;
+    float *part;             // split partials
+    int *counters;           // [pairs], zero between calls
+    int splits, cps, qgroups, pairs;
+};
+
+struct AttnPlan {
+    int qt, qgroups, pairs, splits, cps;
+    size_t part_floats;
+    size_t grid;
+};
+
+AttnPlan plan_attn(int B, int Hkv, int G, int nv, int max_list, int target_wgs);
+hipError_t launch_attn(const AttnArgs &a, int head_dim, int qt, hipStream_t st);
+
+// ---------------------------------------------------------------- scoring
+constexpr int kMaxGroups = 16;
+constexpr int kMaxPairsPerGroup = 64;
+constexpr int kProbTile = 256;    // tokens per workgroup of the softmax-mode logit kernel
+
+struct ScoreGroup {
+    KvView k;
+    int kv_head;
+    int q_head0;      // first query head of the group in q
+    int n_qheads;
+    int pair0;        // first pair of the group in the logit workspace
+    int n_pairs;
+};
+
+struct ScoreArgs {
+    int B, n_max, n_pad, n_groups, n_q, mode, total_qheads, total_pairs, n_tiles, ctx_clamp;
+    const int32_t *ctx_len;
+    const uint16_t *q;
+    double mul;              // PROB_SUM: scale*log2(e) (base-2 logits); LOGIT_SUM2: scale
+    float *logits;           // [B][total_pairs][n_pad]: PROB_SUM l - tile max; LOGIT_SUM2 l
+    double *tile_max;        // PROB_SUM: [B][total_pairs][n_tiles]
+    float *tile_sum;         // PROB_SUM: [B][total_pairs][n_tiles], sum of exp2(l - tile max)
+    float *score;            // [B][n_max]
+    ScoreGroup grp[kMaxGroups];
+};
+
+hipError_t launch_score(const ScoreArgs &a, int head_dim, int max_pairs, hipStream_t st);
+
+// ---------------------------------------------------------------- selection
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectMaxN = 65536;
+
+struct SelectArgs {
+    int B, n_max, k_max;
+    const int32_t *ctx_len;
+    const float *score_draft;   // may be nullptr: no draft tier
+    const float *score_target;
+    const int32_t *budget, *n_sink, *n_window, *m;
+    int32_t *idx, *count;
+};
+
+hipError_t launch_select(const SelectArgs &a, hipStream_t st);
+
+}  // namespace dustin

@@ -1,0 +1,229 @@
+// Hybrid budgeted selection of I_verify (English Dustin summary, "Methodology" 1, last
+// two sentences): sinks and a recent window are always kept, then the top-m tokens by
+// the draft score, then the best remaining tokens by the target score, for a set of
+// fixed size.  Ties go to the smaller position; -0 and +0 compare equal.
+//
+// One workgroup of 1024 threads per sequence.  Thread t owns the contiguous positions
+// [t*E, t*E + E) and keeps their order-preserving 32-bit keys in registers.  Each tier
+// finds its threshold key with a 4-pass 8-bit LDS radix select (histograms are kept
+// per lane slot, with a padded stride, so lanes of one wave never contend for a counter
+// or a bank), takes every eligible key above the threshold plus the first `need` keys
+// equal to it in position order (block-wide exclusive scan), and the final set is
+// compacted in ascending position order with one more block scan.  Integer-only after
+// the key transform, so the result is bit-reproducible.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace dustin {
+
+namespace {
+
+constexpr int kWaves = kSelectThreads / 64;
+constexpr int kCopies = 32;              // lane-slot histogram copies
+constexpr int kHistStride = 257;         // padded so copies sit in different banks
+
+__device__ __forceinline__ uint32_t ord_key(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u)
+        u = 0u;                               // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exclusive scan of one int per thread over the 1024-thread block.
+__device__ int block_scan(int v, int &total, int *sScan)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wid = tid >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o)
+            x += y;
+    }
+    if (lane == 63)
+        sScan[wid] = x;
+    __syncthreads();
+    if (wid == 0) {
+        const int t = lane < kWaves ? sScan[lane] : 0;
+        int y = t;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int z = __shfl_up(y, o);
+            if (lane >= o)
+                y += z;
+        }
+        if (lane < kWaves)
+            sScan[lane] = y - t;
+        if (lane == kWaves - 1)
+            sScan[kWaves] = y;
+    }
+    __syncthreads();
+    const int r = sScan[wid] + x - v;
+    total = sScan[kWaves];
+    __syncthreads();
+    return r;
+}
+
+struct SelShared {
+    uint32_t hist[kCopies * kHistStride];
+    int scan[kWaves + 1];
+    int bcast[2];
+};
+
+// Threshold of the `kth` largest eligible key (1 <= kth <= #eligible): returns the
+// threshold key and, in `need`, how many keys equal to it belong to the top kth.
+template <int E>
+__device__ uint32_t radix_select(const uint32_t (&key)[E], uint64_t elig, int kth, int &need,
+                                 SelShared &sh)
+{
+    const int tid = threadIdx.x;
+    const int slot = (tid & 63) % kCopies;
+    uint32_t prefix = 0;
+    need = kth;
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int i = tid; i < kCopies * kHistStride; i += kSelectThreads)
+            sh.hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool match = pass == 0 || (key[e] >> (shift + 8)) == (prefix >> (shift + 8));
+            if (((elig >> e) & 1) && match)
+                atomicAdd(&sh.hist[slot * kHistStride + ((key[e] >> shift) & 255)], 1u);
+        }
+        __syncthreads();
+        // suffix counts from the top bin down: thread t < 256 holds bin 255 - t
+        int cnt = 0;
+        if (tid < 256) {
+            const int bin = 255 - tid;
+            for (int c = 0; c < kCopies; ++c)
+                cnt += (int)sh.hist[c * kHistStride + bin];
+        }
+        int total;
+        const int before = block_scan(cnt, total, sh.scan);
+        if (tid < 256 && before < need && before + cnt >= need) {
+            sh.bcast[0] = 255 - tid;
+            sh.bcast[1] = need - before;
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sh.bcast[0] << shift;
+        need = sh.bcast[1];
+        __syncthreads();
+    }
+    return prefix;
+}
+
+// Marks the top `kth` eligible keys (threshold + position-ordered ties).
+template <int E>
+__device__ uint64_t take_top(const uint32_t (&key)[E], uint64_t elig, int kth, SelShared &sh)
+{
+    int need;
+    const uint32_t thr = radix_select<E>(key, elig, kth, need, sh);
+    uint64_t sel = 0;
+    int eq = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if ((elig >> e) & 1) {
+            if (key[e] > thr)
+                sel |= 1ull << e;
+            else if (key[e] == thr)
+                ++eq;
+        }
+    }
+    int total;
+    int before = block_scan(eq, total, sh.scan);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        if (((elig >> e) & 1) && key[e] == thr) {
+            if (before < need)
+                sel |= 1ull << e;
+            ++before;
+        }
+    }
+    return sel;
+}
+
+template <int E>
+__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
+{
+    __shared__ SelShared sh;
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int N = clampi(a.ctx_len[b], 0, a.n_max);
+    const int k = clampi(a.budget[b], 0, min(N, a.k_max));
+    int32_t *out = a.idx + (int64_t)b * a.k_max;
+    if (tid == 0)
+        a.count[b] = k;
+    if (k == N) {
+        for (int i = tid; i < a.k_max; i += kSelectThreads)
+            out[i] = i < N ? i : -1;
+        return;
+    }
+    const int s = clampi(a.n_sink[b], 0, k);
+    const int w = clampi(a.n_window[b], 0, k - s);
+    const int md = a.score_draft ? clampi(a.m[b], 0, k - s - w) : 0;
+    const int r = k - s - w - md;
+
+    const int base = tid * E;
+    uint64_t valid = 0, prot = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int t = base + e;
+        if (t < N) {
+            valid |= 1ull << e;
+            if (t < s || t >= N - w)
+                prot |= 1ull << e;
+        }
+    }
+    uint32_t key[E];
+    uint64_t selD = 0, selT = 0;
+    if (md > 0) {
+        const float *sd = a.score_draft + (int64_t)b * a.n_max;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            key[e] = ((valid >> e) & 1) ? ord_key(sd[base + e]) : 0u;
+        selD = take_top<E>(key, valid & ~prot, md, sh);
+    }
+    if (r > 0) {
+        const float *st = a.score_target + (int64_t)b * a.n_max;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            key[e] = ((valid >> e) & 1) ? ord_key(st[base + e]) : 0u;
+        selT = take_top<E>(key, valid & ~prot & ~selD, r, sh);
+    }
+    const uint64_t fin = prot | selD | selT;
+    int total;
+    int o = block_scan(__popcll(fin), total, sh.scan);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (((fin >> e) & 1) && o < a.k_max)
+            out[o++] = base + e;
+    for (int i = k + tid; i < a.k_max; i += kSelectThreads)
+        out[i] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelectArgs &a, hipStream_t st)
+{
+    const int e = (a.n_max + kSelectThreads - 1) / kSelectThreads;
+    const dim3 grid((unsigned)a.B);
+    const dim3 block(kSelectThreads);
+    if (e <= 4)
+        hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, st, a);
+    else if (e <= 8)
+        hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, st, a);
+    else if (e <= 16)
+        hipLaunchKernelGGL(select_kernel<16>, grid, block, 0, st, a);
+    else if (e <= 32)
+        hipLaunchKernelGGL(select_kernel<32>, grid, block, 0, st, a);
+    else
+        hipLaunchKernelGGL(select_kernel<64>, grid, block, 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace dustin

@@ -1,0 +1,239 @@
+"""Python binding of libdustin.so (include/dustin.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels; this module converts torch
+tensors to pointers, strides and sizes, passes torch's current HIP stream, and turns
+non-zero status codes into exceptions.  It never computes a result itself and has no
+fallback: if the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdustin.so")
+
+OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4
+SCORE_PROB_SUM, SCORE_LOGIT_SUM2 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                      "or `python sparse_kv_attention_amd/build.py`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+
+class KvView(ctypes.Structure):
+    _fields_ = [
+        ("base", _P),
+        ("stride_batch", ctypes.c_int64),
+        ("stride_token", ctypes.c_int64),
+        ("stride_head", ctypes.c_int64),
+        ("n_tokens", ctypes.c_int32),
+        ("n_heads", ctypes.c_int32),
+        ("page_table", _P),
+        ("stride_page", ctypes.c_int64),
+        ("page_size", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+    ]
+
+
+class SrhGroup(ctypes.Structure):
+    _fields_ = [("k", KvView), ("kv_head", ctypes.c_int32), ("n_qheads", ctypes.c_int32)]
+
+
+def _decl(name, args):
+    f = getattr(_lib, name)
+    f.argtypes = args
+    f.restype = _I
+    return f
+
+
+_lib.dustin_status_string.argtypes = [_I]
+_lib.dustin_status_string.restype = ctypes.c_char_p
+_score_ws = _decl("dustin_srh_score_workspace_size", [_I, _I, _I, _I, _I, ctypes.POINTER(_SZ)])
+_score = _decl("dustin_srh_score", [_I, _I, _P, _I, ctypes.POINTER(SrhGroup), _I, _P, _I, _F, _I,
+                                    _P, _P, _SZ, _P])
+_select_ws = _decl("dustin_select_workspace_size", [_I, _I, ctypes.POINTER(_SZ)])
+_select = _decl("dustin_select", [_I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _SZ, _P])
+_sparse_ws = _decl("dustin_sparse_verify_attn_workspace_size", [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)])
+_sparse = _decl("dustin_sparse_verify_attn", [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView),
+                                              ctypes.POINTER(KvView), _P, _P, _P, _I, _F, _P, _P, _P,
+                                              _SZ, _P])
+_dense_ws = _decl("dense_verify_attn_workspace_size", [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)])
+_dense = _decl("dense_verify_attn", [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView),
+                                     ctypes.POINTER(KvView), _P, _I, _F, _P, _P, _P, _SZ, _P])
+
+EXPORTED = ("dustin_status_string", "dustin_srh_score_workspace_size", "dustin_srh_score",
+            "dustin_select_workspace_size", "dustin_select",
+            "dustin_sparse_verify_attn_workspace_size", "dustin_sparse_verify_attn",
+            "dense_verify_attn_workspace_size", "dense_verify_attn")
+
+
+class DustinError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.dustin_status_string(status).decode()} ({status})")
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise DustinError(status, where)
+
+
+def status_string(status: int) -> str:
+    return _lib.dustin_status_string(status).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_i32(t: torch.Tensor, name: str):
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 device tensor")
+
+
+def kv_view(cache: torch.Tensor, page_table: Optional[torch.Tensor] = None) -> KvView:
+    """View of a bf16 cache: contiguous [B][n_tokens][Hkv][d], or paged
+    [num_pages][page_size][Hkv][d] with page_table int32 [B][max_pages]."""
+    if cache.dtype != torch.bfloat16 or cache.dim() != 4 or cache.stride(3) != 1 or not cache.is_cuda:
+        raise ValueError("cache must be a 4-d bf16 device tensor with a contiguous last dim")
+    v = KvView()
+    v.base = cache.data_ptr()
+    v.stride_token = cache.stride(1)
+    v.stride_head = cache.stride(2)
+    v.n_heads = cache.shape[2]
+    if page_table is None:
+        v.stride_batch = cache.stride(0)
+        v.n_tokens = cache.shape[1]
+        v.page_table = None
+    else:
+        _dev_i32(page_table, "page_table")
+        v.stride_batch = 0
+        v.n_tokens = 0
+        v.page_table = page_table.data_ptr()
+        v.stride_page = cache.stride(0)
+        v.page_size = cache.shape[1]
+        v.max_pages = page_table.shape[1]
+        v.num_pages = cache.shape[0]
+    return v
+
+
+def workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A zero-filled device workspace of at least `nbytes` (16-byte aligned by torch)."""
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device or "cuda")
+
+
+# ------------------------------------------------------------------------------ scoring
+
+def dustin_srh_score_workspace_size(B: int, n_max: int, total_qheads: int, n_q: int, mode: int) -> int:
+    n = _SZ(0)
+    _check(_score_ws(B, n_max, total_qheads, n_q, mode, ctypes.byref(n)), "dustin_srh_score_workspace_size")
+    return n.value
+
+
+def dustin_srh_score(ctx_len: torch.Tensor, groups: Sequence[Tuple[KvView, int, int]], q: torch.Tensor,
+                     scale: float, mode: int, score: torch.Tensor, ws: torch.Tensor, stream=None):
+    """groups: (kv_view, kv_head, n_qheads) per scored stream; q bf16 [B][sum n_qheads][n_q][d];
+    score fp32 [B][n_max] (written)."""
+    _dev_i32(ctx_len, "ctx_len")
+    B, _, n_q, d = q.shape
+    n_max = score.shape[1]
+    arr = (SrhGroup * len(groups))()
+    for i, (view, kv_head, nqh) in enumerate(groups):
+        arr[i].k = view
+        arr[i].kv_head = kv_head
+        arr[i].n_qheads = nqh
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or score.dtype != torch.float32 or not score.is_contiguous():
+        raise ValueError("q must be contiguous bf16, score contiguous fp32")
+    _check(_score(B, n_max, _ptr(ctx_len), len(groups), arr, d, _ptr(q), n_q, float(scale), mode,
+                  _ptr(score), _ptr(ws), ws.numel(), _stream(stream)), "dustin_srh_score")
+
+
+# ---------------------------------------------------------------------------- selection
+
+def dustin_select_workspace_size(B: int, n_max: int) -> int:
+    n = _SZ(0)
+    _check(_select_ws(B, n_max, ctypes.byref(n)), "dustin_select_workspace_size")
+    return n.value
+
+
+def dustin_select(ctx_len, score_draft, score_target, budget, n_sink, n_window, m, idx, count,
+                  ws: Optional[torch.Tensor] = None, stream=None):
+    """Scores fp32 [B][n_max] (score_draft may be None); per-sequence int32 [B] parameters;
+    idx int32 [B][k_max] and count int32 [B] are written."""
+    for t, n in ((ctx_len, "ctx_len"), (budget, "budget"), (n_sink, "n_sink"), (n_window, "n_window"),
+                 (m, "m"), (idx, "idx"), (count, "count")):
+        _dev_i32(t, n)
+    B, n_max = score_target.shape
+    for s in (score_draft, score_target):
+        if s is not None and (s.dtype != torch.float32 or not s.is_contiguous() or s.shape != (B, n_max)):
+            raise ValueError("scores must be contiguous fp32 [B][n_max]")
+    _check(_select(B, n_max, _ptr(ctx_len), _ptr(score_draft), _ptr(score_target), _ptr(budget),
+                   _ptr(n_sink), _ptr(n_window), _ptr(m), idx.shape[1], _ptr(idx), _ptr(count),
+                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)), "dustin_select")
+
+
+# ---------------------------------------------------------------------------- attention
+
+def dustin_sparse_verify_attn_workspace_size(B, Hq, Hkv, head_dim, n_verify, k_max) -> int:
+    n = _SZ(0)
+    _check(_sparse_ws(B, Hq, Hkv, head_dim, n_verify, k_max, ctypes.byref(n)),
+           "dustin_sparse_verify_attn_workspace_size")
+    return n.value
+
+
+def dense_verify_attn_workspace_size(B, Hq, Hkv, head_dim, n_verify, n_max) -> int:
+    n = _SZ(0)
+    _check(_dense_ws(B, Hq, Hkv, head_dim, n_verify, n_max, ctypes.byref(n)), "dense_verify_attn_workspace_size")
+    return n.value
+
+
+def _attn_common(q, out, lse):
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError("q and out must be contiguous bf16 [B][n_verify][Hq][d]")
+    if out.shape != q.shape or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("out must match q; lse must be contiguous fp32 [B][Hq][n_verify]")
+    B, nv, Hq, d = q.shape
+    if tuple(lse.shape) != (B, Hq, nv):
+        raise ValueError("lse must be [B][Hq][n_verify]")
+    return B, nv, Hq, d
+
+
+def dustin_sparse_verify_attn(q, k: KvView, v: KvView, Hkv: int, ctx_len, idx, count, scale: float,
+                              out, lse, ws, stream=None):
+    B, nv, Hq, d = _attn_common(q, out, lse)
+    _dev_i32(ctx_len, "ctx_len"); _dev_i32(idx, "idx"); _dev_i32(count, "count")
+    _check(_sparse(B, Hq, Hkv, d, nv, _ptr(q), ctypes.byref(k), ctypes.byref(v), _ptr(ctx_len), _ptr(idx),
+                   _ptr(count), idx.shape[1], float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                   _stream(stream)), "dustin_sparse_verify_attn")
+
+
+def dense_verify_attn(q, k: KvView, v: KvView, Hkv: int, ctx_len, n_max: int, scale: float, out, lse, ws,
+                      stream=None):
+    B, nv, Hq, d = _attn_common(q, out, lse)
+    _dev_i32(ctx_len, "ctx_len")
+    _check(_dense(B, Hq, Hkv, d, nv, _ptr(q), ctypes.byref(k), ctypes.byref(v), _ptr(ctx_len), int(n_max),
+                  float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)),
+           "dense_verify_attn")
+
+
+def raw_library():
+    """The loaded ctypes library (for callers that pre-build argument tuples)."""
+    return _lib

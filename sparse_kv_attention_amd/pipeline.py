@@ -1,0 +1,98 @@
+"""One sparse-verification step on device-resident inputs, driven through the C ABI.
+
+Holds the views, workspaces and output buffers of a workload and issues the library
+calls in the order of the verification workflow (English Dustin summary, "Methodology"
+3, steps 2-4): score the draft SRHs, score the target SRHs, select I_verify, then
+verify attention layer by layer.  Argument marshalling only; all arithmetic runs in
+the HIP kernels.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import dustin as D
+from .workloads import Inputs
+
+
+class SparseVerifyStep:
+    def __init__(self, inp: Inputs, layers: Optional[Sequence[int]] = None, logit_sum2: bool = False):
+        self.inp = inp
+        w = inp.w
+        dev = inp.ctx_len.device
+        pt = inp.page_table
+        self.B, self.n_max, self.k_max = w.batch, inp.n_max, inp.k_max
+        self.T, self.Dm = w.target, w.draft
+        self.layers = sorted(inp.k_cache) if layers is None else list(layers)
+        self.logit_sum2 = logit_sum2
+        # a draft signal exists only if the draft speculated at least one token
+        self.has_draft = w.gamma > 0 and not logit_sum2
+        self.draft_groups = [(D.kv_view(inp.draft_k[g.layer], pt), g.kv_head, len(g.qheads))
+                             for g in inp.draft_groups]
+        self.target_groups = [(D.kv_view(inp.k_cache[g.layer], pt), g.kv_head, len(g.qheads))
+                              for g in inp.target_groups]
+        self.kv: Dict[int, tuple] = {l: (D.kv_view(inp.k_cache[l], pt), D.kv_view(inp.v_cache[l], pt))
+                                     for l in inp.k_cache}
+        B, n_max = self.B, self.n_max
+        self.score_draft = torch.zeros((B, n_max), dtype=torch.float32, device=dev)
+        self.score_target = torch.zeros((B, n_max), dtype=torch.float32, device=dev)
+        nd = inp.q_srh_draft.shape[1]
+        nt = inp.q_srh_target.shape[1]
+        mode_t = D.SCORE_LOGIT_SUM2 if logit_sum2 else D.SCORE_PROB_SUM
+        self.mode_t = mode_t
+        ws_score = D.dustin_srh_score_workspace_size(B, n_max, nt, w.n_verify, mode_t)
+        if self.has_draft:
+            ws_score = max(ws_score, D.dustin_srh_score_workspace_size(B, n_max, nd, w.gamma, D.SCORE_PROB_SUM))
+        self.ws_score = D.workspace(ws_score, dev)
+        self.ws_select = D.workspace(D.dustin_select_workspace_size(B, n_max), dev)
+        H = (B, self.T.hq, self.T.hkv, self.T.d, w.n_verify)
+        ws_attn = max(D.dustin_sparse_verify_attn_workspace_size(*H, self.k_max),
+                      D.dense_verify_attn_workspace_size(*H, n_max))
+        self.ws_attn = D.workspace(ws_attn, dev)
+        self.idx = torch.full((B, max(self.k_max, 1)), -1, dtype=torch.int32, device=dev)
+        self.count = torch.zeros((B,), dtype=torch.int32, device=dev)
+        if logit_sum2:
+            zeros = torch.zeros((B,), dtype=torch.int32, device=dev)
+            self.sel_params = (zeros, zeros, zeros)
+        else:
+            self.sel_params = (inp.n_sink, inp.n_window, inp.m)
+        self.scale_draft = 1.0 / math.sqrt(self.Dm.d)
+        self.scale = 1.0 / math.sqrt(self.T.d)
+        self.out = torch.empty((B, w.n_verify, self.T.hq, self.T.d), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((B, self.T.hq, w.n_verify), dtype=torch.float32, device=dev)
+
+    # ---- the stages ----
+    def score(self, stream=None):
+        inp = self.inp
+        if self.has_draft:
+            D.dustin_srh_score(inp.ctx_len, self.draft_groups, inp.q_srh_draft, self.scale_draft,
+                               D.SCORE_PROB_SUM, self.score_draft, self.ws_score, stream)
+        D.dustin_srh_score(inp.ctx_len, self.target_groups, inp.q_srh_target, self.scale,
+                           self.mode_t, self.score_target, self.ws_score, stream)
+
+    def select(self, stream=None):
+        inp = self.inp
+        sink, window, m = self.sel_params
+        D.dustin_select(inp.ctx_len, self.score_draft if self.has_draft else None, self.score_target,
+                        inp.budget, sink, window, m, self.idx, self.count, self.ws_select, stream)
+
+    def attn(self, layer: int, out=None, lse=None, stream=None):
+        k, v = self.kv[layer]
+        D.dustin_sparse_verify_attn(self.inp.q_verify[layer], k, v, self.T.hkv, self.inp.ctx_len, self.idx,
+                                    self.count, self.scale, self.out if out is None else out,
+                                    self.lse if lse is None else lse, self.ws_attn, stream)
+
+    def dense(self, layer: int, out=None, lse=None, stream=None):
+        k, v = self.kv[layer]
+        D.dense_verify_attn(self.inp.q_verify[layer], k, v, self.T.hkv, self.inp.ctx_len, self.n_max,
+                            self.scale, self.out if out is None else out, self.lse if lse is None else lse,
+                            self.ws_attn, stream)
+
+    def step(self, stream=None):
+        """One whole sparse-verification step: both signals, selection, every layer."""
+        self.score(stream)
+        self.select(stream)
+        for l in self.layers:
+            self.attn(l, stream=stream)

@@ -313,7 +313,8 @@ def make_inputs(w: Workload, device="cpu", target_layers: Optional[Sequence[int]
         f = u.pow(-1.0 / w.salience_alpha).clamp_max(w.salience_cap)
         for kc in list(inp.k_cache.values()) + list(inp.draft_k.values()):
             rows = kc.shape[1]
-            kc.copy_((kc.float() * f[:, :rows, None, None]).to(torch.bfloat16))
+            for b in range(B):             # per sequence: no full-size fp32 temporary
+                kc[b].copy_((kc[b].float() * f[b, :rows, None, None]).to(torch.bfloat16))
 
     # ---- planted needles in the SRH streams ----
     if w.needle_mode != "none":

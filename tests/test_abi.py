@@ -1,0 +1,146 @@
+"""The C-ABI library: it loads, exports every function include/dustin.h declares, and
+rejects bad arguments on the host with the documented status (no GPU needed: every
+case here fails validation before anything is enqueued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_kv_attention_amd import dustin as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dustin.h")
+FAKE = 0x10000          # a 16-byte-aligned non-null address; never dereferenced here
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b((?:dustin|dense)_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 9, names
+    assert set(names) == set(D.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", D.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(D.raw_library(), n)
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert D.status_string(s) and D.status_string(s) != "unknown status"
+
+
+def view(**kw):
+    v = D.KvView()
+    v.base, v.stride_batch, v.stride_token, v.stride_head = FAKE, 4 * 1024 * 128, 1024, 128
+    v.n_tokens, v.n_heads = 4096, 8
+    for k, val in kw.items():
+        setattr(v, k, val)
+    return v
+
+
+def sparse(**kw):
+    a = dict(B=2, Hq=64, Hkv=8, d=128, nv=5, q=FAKE, k=view(), v=view(), ctx=FAKE, idx=FAKE, cnt=FAKE,
+             k_max=256, scale=0.1, out=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return D._sparse(a["B"], a["Hq"], a["Hkv"], a["d"], a["nv"], a["q"], ctypes.byref(a["k"]),
+                     ctypes.byref(a["v"]), a["ctx"], a["idx"], a["cnt"], a["k_max"], a["scale"], a["out"],
+                     a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), D.ERR_UNSUPPORTED),
+    (dict(nv=17), D.ERR_UNSUPPORTED),
+    (dict(Hq=60), D.ERR_INVALID_ARG),
+    (dict(Hkv=0), D.ERR_INVALID_ARG),
+    (dict(nv=0), D.ERR_INVALID_ARG),
+    (dict(q=None), D.ERR_INVALID_ARG),
+    (dict(q=FAKE + 2), D.ERR_INVALID_ARG),
+    (dict(out=None), D.ERR_INVALID_ARG),
+    (dict(lse=None), D.ERR_INVALID_ARG),
+    (dict(ctx=None), D.ERR_INVALID_ARG),
+    (dict(idx=None), D.ERR_INVALID_ARG),
+    (dict(cnt=None), D.ERR_INVALID_ARG),
+    (dict(k_max=-1), D.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), D.ERR_INVALID_ARG),
+    (dict(k=view(base=None)), D.ERR_INVALID_ARG),
+    (dict(k=view(stride_token=1001)), D.ERR_INVALID_ARG),
+    (dict(v=view(n_heads=4)), D.ERR_INVALID_ARG),
+    (dict(v=view(n_tokens=3)), D.ERR_INVALID_ARG),
+    (dict(k=view(page_table=FAKE, page_size=12, max_pages=10, num_pages=10, stride_page=4096)), D.ERR_INVALID_ARG),
+    (dict(ws=None), D.ERR_WORKSPACE),
+    (dict(wsb=16), D.ERR_WORKSPACE),
+])
+def test_sparse_attn_rejects(kw, status):
+    assert sparse(**kw) == status
+
+
+def test_zero_batch_is_a_noop():
+    assert sparse(B=0, q=None, out=None) == D.OK
+
+
+def test_dense_rejects():
+    k = view()
+    f = lambda **kw: D._dense(kw.get("B", 2), 64, 8, kw.get("d", 128), 5, FAKE, ctypes.byref(k), ctypes.byref(k),
+                              FAKE, kw.get("n_max", 4000), 0.1, FAKE, FAKE, kw.get("ws", FAKE), kw.get("wsb", 1 << 30), None)
+    assert f(d=64 + 1) == D.ERR_UNSUPPORTED
+    assert f(n_max=-5) == D.ERR_INVALID_ARG
+    assert f(ws=None) == D.ERR_WORKSPACE
+
+
+def test_workspace_queries():
+    n = ctypes.c_size_t(0)
+    assert D._sparse_ws(8, 64, 8, 128, 5, 2048, ctypes.byref(n)) == D.OK and n.value > 0
+    assert D._dense_ws(8, 64, 8, 128, 5, 32768, ctypes.byref(n)) == D.OK and n.value > 0
+    assert D._sparse_ws(8, 64, 8, 96, 5, 2048, ctypes.byref(n)) == D.ERR_UNSUPPORTED
+    assert D._select_ws(8, 32768, ctypes.byref(n)) == D.OK
+    assert D._score_ws(8, 32768, 4, 5, D.SCORE_PROB_SUM, ctypes.byref(n)) == D.OK
+    assert n.value >= 8 * 20 * 32768 * 4
+    assert D._score_ws(8, 32768, 4, 5, 7, ctypes.byref(n)) == D.ERR_INVALID_ARG
+    assert D._score_ws(8, 32768, 4, 0, 0, ctypes.byref(n)) == D.ERR_INVALID_ARG
+
+
+def test_score_rejects():
+    g = (D.SrhGroup * 2)()
+    for i in range(2):
+        g[i].k = view()
+        g[i].kv_head = i
+        g[i].n_qheads = 1
+    f = lambda **kw: D._score(2, kw.get("n_max", 4096), kw.get("ctx", FAKE), kw.get("ng", 2), kw.get("g", g),
+                              kw.get("d", 128), kw.get("q", FAKE), kw.get("nq", 5), 0.1, kw.get("mode", 0),
+                              kw.get("score", FAKE), kw.get("ws", FAKE), kw.get("wsb", 1 << 30), None)
+    assert f(d=32) == D.ERR_UNSUPPORTED
+    assert f(ng=17) == D.ERR_UNSUPPORTED
+    assert f(nq=17) == D.ERR_UNSUPPORTED
+    assert f(ng=0) == D.ERR_INVALID_ARG
+    assert f(mode=5) == D.ERR_INVALID_ARG
+    assert f(q=None) == D.ERR_INVALID_ARG
+    assert f(score=None) == D.ERR_INVALID_ARG
+    assert f(ws=None) == D.ERR_WORKSPACE
+    assert f(wsb=100) == D.ERR_WORKSPACE
+    bad = (D.SrhGroup * 1)()
+    bad[0].k = view()
+    bad[0].kv_head = 8            # the view holds 8 heads: 0..7
+    bad[0].n_qheads = 1
+    assert f(ng=1, g=bad) == D.ERR_INVALID_ARG
+    big = (D.SrhGroup * 1)()
+    big[0].k = view()
+    big[0].kv_head = 0
+    big[0].n_qheads = 13          # 13 heads x 5 queries = 65 pairs > 64
+    assert f(ng=1, g=big) == D.ERR_UNSUPPORTED
+
+
+def test_select_rejects():
+    f = lambda **kw: D._select(2, kw.get("n_max", 4096), FAKE, FAKE, kw.get("st", FAKE), FAKE, FAKE, FAKE,
+                               FAKE, kw.get("k_max", 256), kw.get("idx", FAKE), FAKE, None, 0, None)
+    assert f(n_max=65537) == D.ERR_UNSUPPORTED
+    assert f(st=None) == D.ERR_INVALID_ARG
+    assert f(idx=None) == D.ERR_INVALID_ARG
+    assert f(k_max=-1) == D.ERR_INVALID_ARG

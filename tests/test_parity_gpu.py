@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by element.
+
+Bars: scores within 1e-5 relative (+1e-10 absolute floor; for logit sums the relative
+term is taken against the sum of |logits|), selection bit-exact when the oracle selects
+on the GPU's own fp32 scores, attention output max-abs 2e-2 and LSE 1e-3.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from _harness import (check_attn, check_scores, logit_abs_sum, oracle_attn, oracle_scores,
+                      oracle_select_on, say)
+from oracle import oracle as O
+from sparse_kv_attention_amd import workloads as W
+from sparse_kv_attention_amd.workloads import ModelShape, Workload
+
+pytestmark = pytest.mark.gpu
+
+
+def step_for(inp, layers, logit_sum2=False):
+    from sparse_kv_attention_amd.pipeline import SparseVerifyStep
+    return SparseVerifyStep(inp, layers=layers, logit_sum2=logit_sum2)
+
+
+def check_pipeline(inp, attn_layers, dense_layers, b_attn, b_score=None, logit_sum2=False, b_dense=None):
+    w = inp.w
+    B = w.batch
+    b_score = list(range(B)) if b_score is None else b_score
+    step = step_for(inp, attn_layers, logit_sum2)
+    say(f"[{w.name}] scoring")
+    step.score()
+    torch.cuda.synchronize()
+    sd = step.score_draft.cpu().numpy()
+    st = step.score_target.cpu().numpy()
+    if logit_sum2:
+        ora = oracle_scores(inp, "target", O.LOGIT_SUM2, b_score)
+        check_scores(st[b_score], ora, "target logit-sum scores", cond=logit_abs_sum(inp, "target", b_score))
+    else:
+        if step.has_draft:
+            check_scores(sd[b_score], oracle_scores(inp, "draft", O.PROB_SUM, b_score), "draft scores")
+        check_scores(st[b_score], oracle_scores(inp, "target", O.PROB_SUM, b_score), "target scores")
+    say(f"[{w.name}] selection")
+    step.select()
+    torch.cuda.synchronize()
+    allb = list(range(B))
+    idx_o, cnt_o = oracle_select_on(inp, sd.astype(np.float64) if step.has_draft else None,
+                                    st.astype(np.float64), allb, pure_topk=logit_sum2)
+    idx_g = step.idx.cpu().numpy()
+    cnt_g = step.count.cpu().numpy()
+    assert np.array_equal(cnt_g, cnt_o), (cnt_g, cnt_o)
+    assert np.array_equal(idx_g[:, :inp.k_max], idx_o), "selected positions differ from the oracle's"
+    say(f"  selection bit-exact over {B} sequences (counts {cnt_g.min()}..{cnt_g.max()})")
+    for l in attn_layers:
+        say(f"[{w.name}] sparse attention layer {l}")
+        step.attn(l)
+        torch.cuda.synchronize()
+        check_attn(step.out, step.lse, oracle_attn(inp, l, idx_g, cnt_g, b_attn), b_attn, f"sparse layer {l}")
+    for l in dense_layers:
+        say(f"[{w.name}] dense attention layer {l}")
+        bd = b_attn if b_dense is None else b_dense
+        step.dense(l)
+        torch.cuda.synchronize()
+        check_attn(step.out, step.lse, oracle_attn(inp, l, None, None, bd, dense=True), bd, f"dense layer {l}")
+    return step
+
+
+def small(name, B, n, hq, hkv, d, gamma, budget, s, w, m, seed, dd=64, value_scale=1.0):
+    return Workload(name=name, batch=B, n_ctx=n, target=ModelShape(1, hq, hkv, d),
+                    draft=ModelShape(1, 2, 2, dd), gamma=gamma, budget=budget, n_sink=s, n_window=w, m=m,
+                    srh_draft=((0, 0), (0, 1)), srh_target=((0, 0),), seed=seed, value_scale=value_scale)
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def test_tiny_pipeline():
+    inp = W.make_inputs(W.TINY, device="cuda")
+    step = check_pipeline(inp, [0], [0], [0])
+    # the planted needles carry the largest draft scores: the draft tier must hold them all
+    sel = set(step.idx[0, :int(step.count[0])].tolist())
+    assert set(inp.needles[0].tolist()) <= sel
+
+
+def test_qwen7b_pipeline():
+    inp = W.make_inputs(W.QWEN7B, device="cuda", target_layers=[0])
+    check_pipeline(inp, [0, 20], [0], [0, 1, 2, 3])
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+def test_ragged_and_empty_contexts():
+    w = small("ragged_edges", 5, 700, 8, 2, 128, 3, 96, 4, 16, 24, seed=11)
+    inp = W.make_inputs(w, device="cuda")
+    inp.ctx_len = torch.tensor([0, 1, 50, 97, 700], dtype=torch.int32, device="cuda")
+    step = check_pipeline(inp, [0], [0], [0, 1, 2, 3, 4])
+    assert step.count.cpu().tolist() == [0, 1, 50, 96, 96]
+
+
+def test_full_budget_matches_dense_bitwise():
+    w = small("full_budget", 2, 300, 8, 2, 128, 4, 300, 4, 16, 40, seed=12)
+    inp = W.make_inputs(w, device="cuda")
+    step = check_pipeline(inp, [0], [0], [0, 1])
+    step.attn(0)
+    o_s, l_s = step.out.clone(), step.lse.clone()
+    step.dense(0)
+    assert torch.equal(o_s, step.out) and torch.equal(l_s, step.lse)
+
+
+def test_single_verify_query():
+    w = small("gamma0", 3, 513, 16, 4, 128, 0, 64, 2, 8, 10, seed=13)
+    check_pipeline(W.make_inputs(w, device="cuda"), [0], [0], [0, 1, 2])
+
+
+def test_query_groups_split():
+    # G = 16 query heads per KV head x 8 verify queries = 128 rows: two query groups
+    w = small("qgroups", 2, 400, 32, 2, 128, 7, 100, 4, 8, 20, seed=14)
+    check_pipeline(W.make_inputs(w, device="cuda"), [0], [0], [0, 1])
+
+
+def test_head_dim_64_and_odd_group():
+    w = small("d64", 2, 1000, 14, 2, 64, 4, 200, 4, 32, 50, seed=15)
+    check_pipeline(W.make_inputs(w, device="cuda"), [0], [0], [0, 1])
+
+
+def test_split_plans_agree_and_repeat_bitwise():
+    w = small("splits", 2, 3000, 16, 2, 128, 4, 1024, 16, 64, 300, seed=16)
+    inp = W.make_inputs(w, device="cuda")
+    step = check_pipeline(inp, [0], [], [0, 1])
+    idx, cnt = step.idx.cpu().numpy(), step.count.cpu().numpy()
+    ref = oracle_attn(inp, 0, idx, cnt, [0, 1])
+    refd = oracle_attn(inp, 0, None, None, [0, 1], dense=True)
+    old = os.environ.get("DUSTIN_ATTN_TARGET_WGS")
+    try:
+        for tw in ("1", "7", "100000"):
+            os.environ["DUSTIN_ATTN_TARGET_WGS"] = tw
+            step2 = step_for(inp, [0])
+            step2.idx.copy_(step.idx)
+            step2.count.copy_(step.count)
+            outs = []
+            for _ in range(3):
+                step2.attn(0)
+                outs.append((step2.out.clone(), step2.lse.clone()))
+            torch.cuda.synchronize()
+            for o, l in outs[1:]:
+                assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1]), "not deterministic"
+            check_attn(outs[0][0], outs[0][1], ref, [0, 1], f"sparse, target wgs {tw}")
+            step2.dense(0)
+            torch.cuda.synchronize()
+            check_attn(step2.out, step2.lse, refd, [0, 1], f"dense, target wgs {tw}")
+    finally:
+        if old is None:
+            os.environ.pop("DUSTIN_ATTN_TARGET_WGS", None)
+        else:
+            os.environ["DUSTIN_ATTN_TARGET_WGS"] = old
+
+
+def test_out_of_range_device_values_are_clamped():
+    """Garbage positions and counts cannot make a kernel leave its buffers: the kernel
+    clamps them, and the result is the oracle's on the clamped values."""
+    w = small("clamp", 2, 200, 8, 2, 128, 2, 32, 2, 4, 6, seed=17)
+    inp = W.make_inputs(w, device="cuda")
+    step = step_for(inp, [0])
+    k_max = inp.k_max
+    idx = torch.randint(0, 200, (2, k_max), dtype=torch.int32)
+    idx[0, 3] = -7
+    idx[1, 5] = 10 ** 9
+    cnt = torch.tensor([k_max + 50, 10], dtype=torch.int32)
+    step.idx.copy_(idx)
+    step.count.copy_(cnt)
+    step.attn(0)
+    torch.cuda.synchronize()
+    N = inp.ctx_len.cpu().numpy()
+    idx_c = np.clip(idx.numpy(), 0, N[:, None] - 1).astype(np.int32)
+    cnt_c = np.minimum(cnt.numpy(), k_max).astype(np.int32)
+    check_attn(step.out, step.lse, oracle_attn(inp, 0, idx_c, cnt_c, [0, 1]), [0, 1], "clamped")
+
+
+def test_logit_sum2_pure_topk():
+    w = small("logit2", 3, 2000, 16, 4, 128, 4, 125, 0, 0, 0, seed=18)
+    w = W.shrink(w, srh_target=((0, 0), (0, 1), (0, 4), (0, 8)))
+    inp = W.make_inputs(w, device="cuda")
+    check_pipeline(inp, [0], [], [0, 1, 2], logit_sum2=True)
