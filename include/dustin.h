@@ -102,7 +102,7 @@ const char *dustin_status_string(dustin_status s);
  *   groups : (host) [n_groups], 1 <= n_groups <= 16; all groups share head_dim
  *   q      : bf16 [B][sum of n_qheads][n_q][head_dim], heads in group order
  *   head_dim in {64, 128}; 1 <= n_q <= 16; pairs per group (n_qheads * queries used)
- *   at most 64
+ *   at most 16 in PROB_SUM mode and 64 in LOGIT_SUM2 mode
  *   score  : fp32 [B][n_max], fully written
  *   workspace: at least dustin_srh_score_workspace_size(...) bytes, any contents
  * ------------------------------------------------------------------------------- */
@@ -147,11 +147,10 @@ dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const floa
  *   out[b][t][h] = sum_x softmax_x(scale * q[b][t][h] . K[b][x][g]) V[b][x][g]
  *   lse[b][h][t] = ln sum_x exp(scale * q[b][t][h] . K[b][x][g])
  *   q, out : bf16 [B][n_verify][Hq][head_dim];  lse : fp32 [B][Hq][n_verify]
- *   head_dim in {64, 128}; 1 <= n_verify <= 16; Hq % Hkv == 0
- *   workspace: dustin_sparse_verify_attn_workspace_size(...) bytes.  It holds split
- *   partials and per-(sequence, KV head) counters: it must be zero-filled before its
- *   first use and must not be written by anything else between calls (every call
- *   leaves the counters at zero).
+ *   head_dim in {64, 128}; 1 <= n_verify <= 16; Hq % Hkv == 0;
+ *   k_max + n_verify (dense: n_max + n_verify) <= 131072
+ *   workspace: dustin_sparse_verify_attn_workspace_size(...) bytes, any contents (it
+ *   holds the partial results of the budget splits between the two kernels of a call).
  * dense_verify_attn is the same with I_b = [0, ctx_len[b]); n_max bounds ctx_len.
  * ------------------------------------------------------------------------------- */
 dustin_status dustin_sparse_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_dim,

@@ -61,7 +61,7 @@ int attn_target_wgs(int max_list)
 
 struct AttnWs {
     AttnPlan plan;
-    size_t counters_off, part_off, bytes;
+    size_t part_off, bytes;
 };
 
 AttnWs attn_workspace(int B, int Hq, int Hkv, int n_verify, int max_list)
@@ -69,9 +69,8 @@ AttnWs attn_workspace(int B, int Hq, int Hkv, int n_verify, int max_list)
     AttnWs w;
     const int G = Hq / Hkv;
     w.plan = plan_attn(B, Hkv, G, n_verify, max_list, attn_target_wgs(max_list));
-    w.counters_off = 0;
-    w.part_off = align_up(sizeof(int) * (size_t)w.plan.pairs);
-    w.bytes = w.part_off + align_up(sizeof(float) * w.plan.part_floats);
+    w.part_off = 0;
+    w.bytes = align_up(sizeof(float) * w.plan.part_floats);
     return w;
 }
 
@@ -115,6 +114,8 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
     const int ctx_clamp = std::min(cap - n_verify, sparse ? cap - n_verify : n_max);
     // the split plan depends on host sizes only, exactly as in the workspace-size queries
     const int max_list = (sparse ? k_max : n_max) + n_verify;
+    if (max_list > kMaxSplits * kSplitMax)
+        return DUSTIN_ERR_UNSUPPORTED;
     const AttnWs lay = attn_workspace(B, Hq, Hkv, n_verify, max_list);
     if (lay.bytes > 0 && (!ws || ws_bytes < lay.bytes || !aligned16(ws)))
         return DUSTIN_ERR_WORKSPACE;
@@ -137,13 +138,14 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
     a.scale_log2 = scale * kLog2e;
     a.out = static_cast<uint16_t *>(out);
     a.lse = lse;
-    a.counters = reinterpret_cast<int *>(static_cast<char *>(ws) + lay.counters_off);
     a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.part_off);
     a.splits = lay.plan.splits;
-    a.cps = lay.plan.cps;
+    a.spl = lay.plan.spl;
     a.qgroups = lay.plan.qgroups;
     a.pairs = lay.plan.pairs;
-    const hipError_t e = launch_attn(a, head_dim, lay.plan.qt, static_cast<hipStream_t>(stream));
+    // LDS ring depth per wave: 3 tiles (two in flight) unless overridden for tuning
+    const int ring = env_int("DUSTIN_ATTN_RING", 3);
+    const hipError_t e = launch_attn(a, head_dim, lay.plan.qt, ring, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
 }
 
@@ -217,7 +219,7 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
         const dustin_srh_group &g = groups[i];
         if (g.n_qheads <= 0 || g.kv_head < 0 || !view_ok(&g.k, g.kv_head + 1, 1))
             return DUSTIN_ERR_INVALID_ARG;
-        if (g.n_qheads * ppq > kMaxPairsPerGroup)
+        if (g.n_qheads * ppq > (mode == DUSTIN_SCORE_PROB_SUM ? kMaxProbPairsPerGroup : kMaxPairsPerGroup))
             return DUSTIN_ERR_UNSUPPORTED;
         total_qheads += g.n_qheads;
         max_pairs = std::max(max_pairs, g.n_qheads * ppq);
@@ -311,6 +313,8 @@ dustin_status dustin_sparse_verify_attn_workspace_size(int B, int Hq, int Hkv, i
         return DUSTIN_ERR_INVALID_ARG;
     if (!attn_shape_ok(B, Hq, Hkv, head_dim, n_verify, st))
         return st;
+    if (k_max + n_verify > kMaxSplits * kSplitMax)
+        return DUSTIN_ERR_UNSUPPORTED;
     *bytes = attn_workspace(B, Hq, Hkv, n_verify, k_max + n_verify).bytes;
     return DUSTIN_OK;
 }
@@ -336,6 +340,8 @@ dustin_status dense_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_
         return DUSTIN_ERR_INVALID_ARG;
     if (!attn_shape_ok(B, Hq, Hkv, head_dim, n_verify, st))
         return st;
+    if (n_max + n_verify > kMaxSplits * kSplitMax)
+        return DUSTIN_ERR_UNSUPPORTED;
     *bytes = attn_workspace(B, Hq, Hkv, n_verify, n_max + n_verify).bytes;
     return DUSTIN_OK;
 }

@@ -10,7 +10,9 @@
 namespace dustin {
 
 // ---------------------------------------------------------------- attention
-constexpr int kMaxQT = 5;   // 16-row query tiles held by one workgroup
+constexpr int kMaxQT = 5;        // 16-row query tiles held by one workgroup
+constexpr int kSplitMax = 1024;  // list positions of one workgroup (its LDS token table)
+constexpr int kMaxSplits = 128;  // splits of one (sequence, KV head, query group)
 
 struct AttnArgs {
     int B, Hq, Hkv, G, nv, GV;
@@ -25,22 +27,22 @@ struct AttnArgs {
     uint16_t *out;
     float *lse;
     float *part;             // split partials
-    int *counters;           // [pairs], zero between calls
-    int splits, cps, qgroups, pairs;
+    int splits, spl, qgroups, pairs;   // spl: list positions per split
 };
 
 struct AttnPlan {
-    int qt, qgroups, pairs, splits, cps;
+    int qt, qgroups, pairs, splits, spl;
     size_t part_floats;
     size_t grid;
 };
 
 AttnPlan plan_attn(int B, int Hkv, int G, int nv, int max_list, int target_wgs);
-hipError_t launch_attn(const AttnArgs &a, int head_dim, int qt, hipStream_t st);
+hipError_t launch_attn(const AttnArgs &a, int head_dim, int qt, int ring, hipStream_t st);
 
 // ---------------------------------------------------------------- scoring
 constexpr int kMaxGroups = 16;
-constexpr int kMaxPairsPerGroup = 64;
+constexpr int kMaxPairsPerGroup = 64;       // logit-sum mode
+constexpr int kMaxProbPairsPerGroup = 16;   // softmax mode
 constexpr int kProbTile = 256;    // tokens per workgroup of the softmax-mode logit kernel
 
 struct ScoreGroup {

@@ -29,7 +29,7 @@ namespace dustin {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPairChunk = 8;              // pairs per pass of the fp64 kernel
+constexpr int kProbTilesPerWg = 4;         // tiles each softmax-mode workgroup streams
 
 __device__ __forceinline__ double wave_max_f64(double v)
 {
@@ -47,69 +47,83 @@ __device__ __forceinline__ float wave_sum_f32(float v)
     return v;
 }
 
-template <int D>
+template <int D, int PC>
 __global__ __launch_bounds__(kThreads) void srh_prob_logits_kernel(ScoreArgs a)
 {
     constexpr int RB = D * 2;          // bytes per key row
     constexpr int RSTR = RB + 16;      // LDS row stride (conflict-free 16-byte row reads)
     constexpr int CPR = RB / 16;       // 16-byte chunks per row
+    constexpr int LPT = kProbTile * CPR / kThreads;   // 16-byte loads per thread per tile
     __shared__ __align__(16) uint8_t sK[kProbTile * RSTR];
-    __shared__ __align__(16) double sQ[kPairChunk][D];
-    __shared__ double sMx[4][kPairChunk];
-    __shared__ float sSm[4][kPairChunk];
+    __shared__ __align__(16) double sQ[PC][D];
+    __shared__ double sMx[4][PC];
+    __shared__ float sSm[4][PC];
 
-    const int tile = blockIdx.x;
     const ScoreGroup &G = a.grp[blockIdx.y];
     const int b = blockIdx.z;
     const int N = clampi(a.ctx_len[b], 0, a.ctx_clamp);
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
-    const int t0 = tile * kProbTile;
-    const int tok = t0 + tid;
-    const bool valid = tok < N;
-    const int64_t stat0 = ((int64_t)b * a.total_pairs + G.pair0) * a.n_tiles + tile;
+    const int n_live = (N + kProbTile - 1) / kProbTile;     // tiles holding context tokens
 
-    if (t0 >= N) {                     // nothing to score: an empty partial
+    // tiles past the context: empty partials
+    for (int tile = n_live + blockIdx.x; tile < a.n_tiles; tile += gridDim.x)
         for (int p = tid; p < G.n_pairs; p += kThreads) {
-            a.tile_max[stat0 + (int64_t)p * a.n_tiles] = -INFINITY;
-            a.tile_sum[stat0 + (int64_t)p * a.n_tiles] = 0.f;
+            const int64_t st = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_tiles + tile;
+            a.tile_max[st] = -INFINITY;
+            a.tile_sum[st] = 0.f;
         }
+    if ((int)blockIdx.x >= n_live)
         return;
-    }
 
-    // ---- the tile's key rows, coalesced, into LDS ----
-    for (int c = tid; c < kProbTile * CPR; c += kThreads) {
-        const int r = c / CPR;
-        const int ch = c - r * CPR;
-        const int t = t0 + r;
-        u32x4 v{0, 0, 0, 0};
-        if (t < N)
-            v = load16(G.k.base + kv_offset(G.k, b, t, G.kv_head) + ch * 8);
-        *reinterpret_cast<u32x4 *>(&sK[r * RSTR + ch * 16]) = v;
-    }
-
-    const uint8_t *row = &sK[tid * RSTR];
-    for (int pc0 = 0; pc0 < G.n_pairs; pc0 += kPairChunk) {
-        __syncthreads();               // key rows staged / previous chunk's sQ consumed
-        for (int e = tid; e < kPairChunk * D; e += kThreads) {
-            const int p = e / D;
-            const int dd = e - p * D;
-            const int pair = pc0 + p;
-            double qv = 0.0;
-            if (pair < G.n_pairs) {
-                const int hl = pair / a.n_q;
-                const int j = pair - hl * a.n_q;
-                const uint16_t h = a.q[((int64_t)(b * a.total_qheads + G.q_head0 + hl) * a.n_q + j) * D + dd];
-                qv = (double)__uint_as_float((uint32_t)h << 16);
-            }
-            sQ[p][dd] = qv;
+    // the group's queries (fp64) stay in LDS for every tile of this workgroup
+    for (int e = tid; e < PC * D; e += kThreads) {
+        const int p = e / D;
+        const int dd = e - p * D;
+        double qv = 0.0;
+        if (p < G.n_pairs) {
+            const int hl = p / a.n_q;
+            const int j = p - hl * a.n_q;
+            const uint16_t h = a.q[((int64_t)(b * a.total_qheads + G.q_head0 + hl) * a.n_q + j) * D + dd];
+            qv = (double)__uint_as_float((uint32_t)h << 16);
         }
+        sQ[p][dd] = qv;
+    }
+
+    // tile rows: thread tid loads chunks tid + i*256 (row = chunk / CPR), all issued at once
+    u32x4 kr[LPT];
+    auto issue = [&](int tile) {
+        const int t0 = tile * kProbTile;
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int c = tid + i * kThreads;
+            const int r = c / CPR;
+            const int t = t0 + r;
+            kr[i] = t < N ? load16(G.k.base + kv_offset(G.k, b, t, G.kv_head) + (c - r * CPR) * 8)
+                          : u32x4{0, 0, 0, 0};
+        }
+    };
+    int tile = blockIdx.x;
+    issue(tile);
+    for (; tile < n_live; tile += gridDim.x) {
+        __syncthreads();                  // previous tile's rows consumed
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int c = tid + i * kThreads;
+            const int r = c / CPR;
+            *reinterpret_cast<u32x4 *>(&sK[r * RSTR + (c - r * CPR) * 16]) = kr[i];
+        }
+        if (tile + (int)gridDim.x < n_live)
+            issue(tile + gridDim.x);      // next tile in flight during this tile's math
         __syncthreads();
 
-        double acc[kPairChunk];
+        const int tok = tile * kProbTile + tid;
+        const bool valid = tok < N;
+        const uint8_t *row = &sK[tid * RSTR];
+        double acc[PC];
 #pragma unroll
-        for (int p = 0; p < kPairChunk; ++p)
+        for (int p = 0; p < PC; ++p)
             acc[p] = 0.0;
 #pragma unroll 2
         for (int dd = 0; dd < D; dd += 8) {
@@ -121,41 +135,39 @@ __global__ __launch_bounds__(kThreads) void srh_prob_logits_kernel(ScoreArgs a)
                 kv[2 * j + 1] = (double)bf16_hi(kw[j]);
             }
 #pragma unroll
-            for (int p = 0; p < kPairChunk; ++p)
+            for (int p = 0; p < PC; ++p)
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     acc[p] = fma(kv[j], sQ[p][dd + j], acc[p]);
         }
 
-        // ---- per-pair tile maximum (fp64), offsets, sum of exp2 ----
-        double l[kPairChunk];
+        // ---- per-pair tile maximum (fp64), offsets from it, sum of exp2 ----
+        double l[PC];
 #pragma unroll
-        for (int p = 0; p < kPairChunk; ++p) {
+        for (int p = 0; p < PC; ++p) {
             l[p] = valid ? acc[p] * a.mul : -INFINITY;
             const double m = wave_max_f64(l[p]);
             if (lane == 0)
                 sMx[w][p] = m;
         }
         __syncthreads();
-        float off[kPairChunk];
 #pragma unroll
-        for (int p = 0; p < kPairChunk; ++p) {
+        for (int p = 0; p < PC; ++p) {
             const double m = fmax(fmax(sMx[0][p], sMx[1][p]), fmax(sMx[2][p], sMx[3][p]));
-            off[p] = valid ? (float)(l[p] - m) : -INFINITY;
-            const float s = wave_sum_f32(valid ? fast_exp2(off[p]) : 0.f);
+            const float off = valid ? (float)(l[p] - m) : -INFINITY;
+            const float s = wave_sum_f32(valid ? fast_exp2(off) : 0.f);
             if (lane == 0)
                 sSm[w][p] = s;
-            const int pair = pc0 + p;
-            if (valid && pair < G.n_pairs)
-                a.logits[((int64_t)b * a.total_pairs + G.pair0 + pair) * a.n_pad + tok] = off[p];
+            if (valid && p < G.n_pairs)
+                a.logits[((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_pad + tok] = off;
         }
         __syncthreads();
-        if (tid < kPairChunk && pc0 + tid < G.n_pairs) {
+        if (tid < G.n_pairs && tid < PC) {
             const int p = tid;
             const double m = fmax(fmax(sMx[0][p], sMx[1][p]), fmax(sMx[2][p], sMx[3][p]));
-            const float s = (sSm[0][p] + sSm[1][p]) + (sSm[2][p] + sSm[3][p]);
-            a.tile_max[stat0 + (int64_t)(pc0 + p) * a.n_tiles] = m;
-            a.tile_sum[stat0 + (int64_t)(pc0 + p) * a.n_tiles] = s;
+            const int64_t st = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_tiles + tile;
+            a.tile_max[st] = m;
+            a.tile_sum[st] = (sSm[0][p] + sSm[1][p]) + (sSm[2][p] + sSm[3][p]);
         }
     }
 }
@@ -325,25 +337,45 @@ hipError_t launch_logit_sum(const ScoreArgs &a, int pt, dim3 grid, hipStream_t s
     return hipGetLastError();
 }
 
+// the softmax-mode kernel, instantiated for the pair counts of one group
+template <int D>
+hipError_t launch_prob(const ScoreArgs &a, int max_pairs, dim3 grid, hipStream_t st)
+{
+    if (max_pairs <= 4)
+        hipLaunchKernelGGL((srh_prob_logits_kernel<D, 4>), grid, dim3(kThreads), 0, st, a);
+    else if (max_pairs <= 5)
+        hipLaunchKernelGGL((srh_prob_logits_kernel<D, 5>), grid, dim3(kThreads), 0, st, a);
+    else if (max_pairs <= 8)
+        hipLaunchKernelGGL((srh_prob_logits_kernel<D, 8>), grid, dim3(kThreads), 0, st, a);
+    else if (max_pairs <= 16)
+        hipLaunchKernelGGL((srh_prob_logits_kernel<D, 16>), grid, dim3(kThreads), 0, st, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_score(const ScoreArgs &a, int head_dim, int max_pairs, hipStream_t st)
 {
+    hipError_t e = hipSuccess;
     if (a.mode == DUSTIN_SCORE_PROB_SUM) {
-        const dim3 g1((unsigned)a.n_tiles, (unsigned)a.n_groups, (unsigned)a.B);
+        const dim3 g1((unsigned)((a.n_tiles + kProbTilesPerWg - 1) / kProbTilesPerWg), (unsigned)a.n_groups,
+                      (unsigned)a.B);
         if (head_dim == 64)
-            hipLaunchKernelGGL(srh_prob_logits_kernel<64>, g1, dim3(kThreads), 0, st, a);
+            e = launch_prob<64>(a, max_pairs, g1, st);
         else
-            hipLaunchKernelGGL(srh_prob_logits_kernel<128>, g1, dim3(kThreads), 0, st, a);
+            e = launch_prob<128>(a, max_pairs, g1, st);
+        if (e != hipSuccess)
+            return e;
     } else {
         const dim3 g1((unsigned)((a.n_max + kSumTile - 1) / kSumTile), (unsigned)a.n_groups, (unsigned)a.B);
         const int pt = (max_pairs + 15) / 16;
-        const hipError_t e = head_dim == 64 ? launch_logit_sum<64>(a, pt, g1, st)
-                                            : launch_logit_sum<128>(a, pt, g1, st);
+        e = head_dim == 64 ? launch_logit_sum<64>(a, pt, g1, st) : launch_logit_sum<128>(a, pt, g1, st);
         if (e != hipSuccess)
             return e;
     }
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     const dim3 g2((unsigned)((a.n_max + kFinTokens - 1) / kFinTokens), (unsigned)a.B);

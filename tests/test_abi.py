@@ -133,8 +133,10 @@ def test_score_rejects():
     big = (D.SrhGroup * 1)()
     big[0].k = view()
     big[0].kv_head = 0
-    big[0].n_qheads = 13          # 13 heads x 5 queries = 65 pairs > 64
+    big[0].n_qheads = 4           # 4 heads x 5 queries = 20 softmax pairs > 16
     assert f(ng=1, g=big) == D.ERR_UNSUPPORTED
+    big[0].n_qheads = 33          # 33 heads x 2 queries = 66 logit-sum pairs > 64
+    assert f(ng=1, g=big, mode=1) == D.ERR_UNSUPPORTED
 
 
 def test_select_rejects():
