@@ -51,12 +51,28 @@ int env_int(const char *name, int dflt)
     return v > 0 ? v : dflt;
 }
 
-// Target number of attention workgroups per launch (about 2 resident per CU on 256 CUs,
-// more for long lists so the tail of the grid balances).
-int attn_target_wgs(int max_list)
+// Compute units of the current device (cached per device id).
+int device_cus()
 {
-    const int dflt = max_list > 8192 ? 2048 : 512;
-    return env_int("DUSTIN_ATTN_TARGET_WGS", dflt);
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+// Workgroups per round of the attention grid: one resident workgroup per CU (the
+// per-wave tile rings take most of the LDS).  The split count is rounded so the grid is
+// a whole number of rounds.
+int attn_target_wgs()
+{
+    return env_int("DUSTIN_ATTN_TARGET_WGS", device_cus());
 }
 
 struct AttnWs {
@@ -64,14 +80,31 @@ struct AttnWs {
     size_t part_off, bytes;
 };
 
-AttnWs attn_workspace(int B, int Hq, int Hkv, int n_verify, int max_list)
+// Positions one attention workgroup can hold: its LDS offset table is shared by K and V
+// when their rows sit at the same offsets, else halved between them.
+int attn_split_cap(bool kv_same) { return kv_same ? kSplitMax : 1024; }
+
+AttnWs attn_workspace(int B, int Hq, int Hkv, int n_verify, int max_list, bool kv_same)
 {
     AttnWs w;
     const int G = Hq / Hkv;
-    w.plan = plan_attn(B, Hkv, G, n_verify, max_list, attn_target_wgs(max_list));
+    w.plan = plan_attn(B, Hkv, G, n_verify, max_list, attn_target_wgs(), attn_split_cap(kv_same));
     w.part_off = 0;
     w.bytes = align_up(sizeof(float) * w.plan.part_floats);
     return w;
+}
+
+// Workspace bytes valid for either table layout (the size queries do not see the views).
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int n_verify, int max_list)
+{
+    return std::max(attn_workspace(B, Hq, Hkv, n_verify, max_list, true).bytes,
+                    attn_workspace(B, Hq, Hkv, n_verify, max_list, false).bytes);
+}
+
+bool same_rows(const KvView &k, const KvView &v)
+{
+    return k.sb == v.sb && k.st == v.st && k.sp == v.sp && k.pt == v.pt && k.ps_log2 == v.ps_log2 &&
+           k.max_pages == v.max_pages && k.num_pages == v.num_pages;
 }
 
 bool attn_shape_ok(int B, int Hq, int Hkv, int head_dim, int n_verify, dustin_status &st)
@@ -114,9 +147,11 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
     const int ctx_clamp = std::min(cap - n_verify, sparse ? cap - n_verify : n_max);
     // the split plan depends on host sizes only, exactly as in the workspace-size queries
     const int max_list = (sparse ? k_max : n_max) + n_verify;
-    if (max_list > kMaxSplits * kSplitMax)
+    if (max_list > kMaxList)
         return DUSTIN_ERR_UNSUPPORTED;
-    const AttnWs lay = attn_workspace(B, Hq, Hkv, n_verify, max_list);
+    const KvView kv = make_view(*k), vv = make_view(*v);
+    const bool kv_same = same_rows(kv, vv);
+    const AttnWs lay = attn_workspace(B, Hq, Hkv, n_verify, max_list, kv_same);
     if (lay.bytes > 0 && (!ws || ws_bytes < lay.bytes || !aligned16(ws)))
         return DUSTIN_ERR_WORKSPACE;
 
@@ -128,8 +163,9 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
     a.nv = n_verify;
     a.GV = a.G * n_verify;
     a.q = static_cast<const uint16_t *>(q);
-    a.k = make_view(*k);
-    a.v = make_view(*v);
+    a.k = kv;
+    a.v = vv;
+    a.kv_same = kv_same ? 1 : 0;
     a.ctx_len = ctx_len;
     a.idx = sparse ? idx : nullptr;
     a.count = sparse ? count : nullptr;
@@ -143,7 +179,7 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
     a.spl = lay.plan.spl;
     a.qgroups = lay.plan.qgroups;
     a.pairs = lay.plan.pairs;
-    // LDS ring depth per wave: 3 tiles (two in flight) unless overridden for tuning
+    // LDS ring depth per wave for head dim 64 (head dim 128 always uses two slots)
     const int ring = env_int("DUSTIN_ATTN_RING", 3);
     const hipError_t e = launch_attn(a, head_dim, lay.plan.qt, ring, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
@@ -313,9 +349,9 @@ dustin_status dustin_sparse_verify_attn_workspace_size(int B, int Hq, int Hkv, i
         return DUSTIN_ERR_INVALID_ARG;
     if (!attn_shape_ok(B, Hq, Hkv, head_dim, n_verify, st))
         return st;
-    if (k_max + n_verify > kMaxSplits * kSplitMax)
+    if (k_max + n_verify > kMaxList)
         return DUSTIN_ERR_UNSUPPORTED;
-    *bytes = attn_workspace(B, Hq, Hkv, n_verify, k_max + n_verify).bytes;
+    *bytes = attn_workspace_bytes(B, Hq, Hkv, n_verify, k_max + n_verify);
     return DUSTIN_OK;
 }
 
@@ -340,9 +376,9 @@ dustin_status dense_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_
         return DUSTIN_ERR_INVALID_ARG;
     if (!attn_shape_ok(B, Hq, Hkv, head_dim, n_verify, st))
         return st;
-    if (n_max + n_verify > kMaxSplits * kSplitMax)
+    if (n_max + n_verify > kMaxList)
         return DUSTIN_ERR_UNSUPPORTED;
-    *bytes = attn_workspace(B, Hq, Hkv, n_verify, n_max + n_verify).bytes;
+    *bytes = attn_workspace_bytes(B, Hq, Hkv, n_verify, n_max + n_verify);
     return DUSTIN_OK;
 }
 

@@ -33,18 +33,14 @@ namespace dustin {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kTile = 32;          // list positions per wave step
 constexpr float kLazy = 8.f;       // rescale O only when a tile's max exceeds the reference by 2^8
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ f32x4 mfma_bf16_k16(u32x2 a, u32x2 b, f32x4 c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                      __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
-}
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
@@ -60,37 +56,90 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// max over the four lanes l, l^16, l^32, l^48 (v_permlane32_swap / v_permlane16_swap)
+__device__ __forceinline__ float max_over_quads(float x)
+{
+    const uint32_t u = __float_as_uint(x);
+    const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const uint32_t v = __float_as_uint(y);
+    const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// LDS transposing read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i receives
+// 16-bit element i % 4 of the 8-byte words addressed by lanes i / 4, 4 + i / 4, 8 + i / 4
+// and 12 + i / 4 of its group, in that order.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t *p)
+{
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Geometry of one wave step for head dim D.  A step covers kTile list positions; its K
+// rows and V rows are each moved into LDS by NI DMA instructions of 64 lanes x 16 bytes,
+// instruction n covering LDS rows n*RPI .. n*RPI + RPI - 1 with whole rows per lane group
+// (fully coalesced reads).  LDS row rho holds list row tau(rho) = (rho % RPI) * NI +
+// rho / RPI of the step, so the NI rows one lane moves are consecutive list positions.
+// Chunks (16 bytes) of a row are stored XOR-swizzled: K chunk c of row rho sits at
+// c ^ (rho % CPR), V chunk c at c ^ (2 rho % CPR), which makes the MFMA operand reads
+// (K: 16 rows x one chunk; V transposed: 8 rows x two chunks per half-wave) bank-conflict free.
+template <int D>
+struct Geo {
+    static constexpr int RB = 2 * D;            // bytes of one row of one head
+    static constexpr int CPR = RB / 16;         // 16-byte chunks per row
+    static constexpr int RPI = 1024 / RB;       // rows per DMA instruction
+    static constexpr int NI = kTile / RPI;      // DMA instructions per tensor per step
+    static constexpr int KS = D / 32;           // k-steps of QK^T (16x16x32)
+    static constexpr int DVT = D / 16;          // 16-wide head-dim tiles of PV
+    static constexpr int HALF = kTile * RB;     // bytes of the K (or V) rows of a step
+    static constexpr int SLOT = 2 * HALF;
+    __device__ static constexpr int tau(int rho) { return (rho % RPI) * NI + rho / RPI; }
+};
+
 template <int D, int QT, int R>
 struct AttnShape {
-    static constexpr int KS = D / 32;          // 16x16x32 k-steps of QK = 16-byte loads per row quarter
-    static constexpr int QD = D / 4;           // head-dim quarter held by one MFMA lane group
-    static constexpr int DVT = D / 16;         // 16-wide head-dim tiles of PV
-    static constexpr int QR = QT * 16;         // padded query rows
-    static constexpr int SLOT = 2 * KS * 1024; // one ring slot: KS KB of K rows, then KS KB of V rows
-    static constexpr int ACC = DVT * QT * 4;   // O accumulator floats per lane
-    static constexpr int TAB = kSplitMax * 4 * 3;
-    static constexpr int RING = 4 * R * SLOT;
-    static constexpr int MRG = 64 * ACC * 4 + 2 * QR * 4;
+    using G = Geo<D>;
+    static constexpr int QR = QT * 16;          // padded query rows
+    static constexpr int ACC = G::DVT * QT * 4; // O accumulator floats per lane
+    static constexpr int TAB = kSplitMax * 8;
+    static constexpr int RING = 4 * R * G::SLOT;
+    static constexpr int MRG = 4 * 64 * ACC * 4 + 2 * 4 * QR * 4;
     static constexpr int LDS = TAB + (RING > MRG ? RING : MRG);
+    static_assert(LDS <= 160 * 1024, "LDS budget");
 };
+
+// Element offset of token t's row (head 0) in a view; t lies in [0, cap).
+__device__ __forceinline__ int64_t row_offset(const KvView &v, int b, int t)
+{
+    if (v.pt) {
+        const int pg = clampi(v.pt[(int64_t)b * v.max_pages + (t >> v.ps_log2)], 0, v.num_pages - 1);
+        return (int64_t)pg * v.sp + (int64_t)(t & ((1 << v.ps_log2) - 1)) * v.st;
+    }
+    return (int64_t)b * v.sb + (int64_t)t * v.st;
+}
 
 template <int D, int QT, int R>
 __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
 {
     using S = AttnShape<D, QT, R>;
+    using G = Geo<D>;
     __shared__ __align__(16) uint8_t lds[S::LDS];
-    int *sTok = reinterpret_cast<int *>(lds);
-    int *sPgK = sTok + kSplitMax;
-    int *sPgV = sPgK + kSplitMax;
+    int64_t *sOffK = reinterpret_cast<int64_t *>(lds);
+    int64_t *sOffV = a.kv_same ? sOffK : sOffK + kSplitMax / 2;
 
-    // ---- block -> (pair, split); all splits of a pair share blockIdx % 8 (one XCD) ----
+    // ---- block -> (sequence, KV head, query group, split).  Every workgroup of one
+    //      (sequence, KV head) has the same blockIdx % 8, i.e. runs on the same XCD, so
+    //      the query groups re-reading its rows find them in that XCD's L2 ----
     const int x = blockIdx.x;
-    const int pair = ((x >> 3) / a.splits) * 8 + (x & 7);
-    const int split = (x >> 3) % a.splits;
-    if (pair >= a.pairs)
+    const int hi = x >> 3;
+    const int split = hi % a.splits;
+    const int t2 = hi / a.splits;
+    const int qg = t2 % a.qgroups;
+    const int bg = (t2 / a.qgroups) * 8 + (x & 7);
+    if (bg >= a.B * a.Hkv)
         return;
-    const int qg = pair % a.qgroups;
-    const int bg = pair / a.qgroups;
+    const int pair = bg * a.qgroups + qg;
     const int g = bg % a.Hkv;
     const int b = bg / a.Hkv;
 
@@ -99,342 +148,396 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
     const int lane = tid & 63;
     const int quad = lane >> 4;   // MFMA lane group
     const int li = lane & 15;
-
-    // ---- sequence geometry; every device value is clamped ----
-    const int N = clampi(a.ctx_len[b], 0, a.ctx_clamp);
-    const int nsel = a.idx ? clampi(a.count[b], 0, min(a.k_max, N)) : N;
-    const int L = nsel + a.nv;
     const int p0 = split * a.spl;
-    const int p1 = min(p0 + a.spl, L);
-    const int cnt = max(p1 - p0, 0);
-    const int full_end = min(p1, nsel);   // positions below this need no mask
 
-    // ---- the split's tokens (and pages) into LDS: index loads first, then pages ----
-    {
-        int raw[kSplitMax / kThreads];
+    // ---- one round trip: the split's index entries, the sequence's length and count,
+    //      and Q; none of these loads depends on another ----
+    constexpr int PT = (kSplitMax + kThreads - 1) / kThreads;
+    int raw[PT];
 #pragma unroll
-        for (int k = 0; k < kSplitMax / kThreads; ++k) {
-            const int i = tid + k * kThreads;
-            const int pos = p0 + i;
-            raw[k] = (i < cnt && a.idx && pos < nsel) ? a.idx[(int64_t)b * a.k_max + pos] : 0;
-        }
-#pragma unroll
-        for (int k = 0; k < kSplitMax / kThreads; ++k) {
-            const int i = tid + k * kThreads;
-            if (i >= cnt)
-                continue;
-            const int pos = p0 + i;
-            const int tok = pos < nsel ? (a.idx ? clampi(raw[k], 0, N - 1) : pos) : N + (pos - nsel);
-            sTok[i] = tok;
-            if (a.k.pt)
-                sPgK[i] = clampi(a.k.pt[(int64_t)b * a.k.max_pages + (tok >> a.k.ps_log2)], 0, a.k.num_pages - 1);
-            if (a.v.pt)
-                sPgV[i] = clampi(a.v.pt[(int64_t)b * a.v.max_pages + (tok >> a.v.ps_log2)], 0, a.v.num_pages - 1);
-        }
+    for (int k = 0; k < PT; ++k) {
+        const int i = tid + k * kThreads;
+        const int pos = p0 + i;
+        raw[k] = (a.idx && i < a.spl && pos < a.k_max) ? a.idx[(int64_t)b * a.k_max + pos] : 0;
     }
+    const int n_raw = a.ctx_len[b];
+    const int c_raw = a.idx ? a.count[b] : 0;
 
-    // ---- Q as the B operand of S^T = K Q^T: lane holds q-row (qt*16 + li), its quarter
-    //      of the head dim; k-step ks covers elements quad*D/4 + ks*8 .. +8 ----
-    u32x4 qop[QT][S::KS];
+    // Q as the B operand of S^T = K Q^T: lane holds q-row qt*16 + li, head-dim elements
+    // ks*32 + quad*8 .. +8 for k-step ks.  A negative scale is moved into Q (exact sign
+    // flip), so the kernel only ever multiplies logits by c = |scale| log2(e) >= 0.  Q is
+    // loaded after the first K/V step has been requested (it is needed only by the math).
+    const float c = fmaxf(fabsf(a.scale_log2), 1e-30f);
+    const uint32_t qsign = a.scale_log2 < 0.f ? 0x80008000u : 0u;
+    u32x4 qop[QT][G::KS];
     int qrow_t[QT];   // verify index t of the lane's query row (large for padding rows)
+    const uint16_t *qptr[QT];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         const int row = qg * S::QR + qt * 16 + li;
+        qrow_t[qt] = 1 << 20;
+        qptr[qt] = nullptr;
         if (row < a.GV) {
             const int t = row / a.G;
             const int h = g * a.G + (row - t * a.G);
-            const uint16_t *p = a.q + ((int64_t)(b * a.nv + t) * a.Hq + h) * D + quad * S::QD;
-#pragma unroll
-            for (int ks = 0; ks < S::KS; ++ks)
-                qop[qt][ks] = load16(p + ks * 8);
+            qptr[qt] = a.q + ((int64_t)(b * a.nv + t) * a.Hq + h) * D + quad * 8;
             qrow_t[qt] = t;
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < S::KS; ++ks)
-                qop[qt][ks] = u32x4{0, 0, 0, 0};
-            qrow_t[qt] = 1 << 20;
         }
     }
-    __syncthreads();                  // token table ready
-
-    f32x4 acc[S::DVT][QT];
+    auto load_q = [&]() {
 #pragma unroll
-    for (int i = 0; i < S::DVT; ++i)
+        for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks)
+                qop[qt][ks] = qptr[qt] ? (load16(qptr[qt] + ks * 32) ^ qsign) : u32x4{0, 0, 0, 0};
+    };
+
+    // ---- sequence geometry; every device value is clamped ----
+    const int N = clampi(n_raw, 0, a.ctx_clamp);
+    const int nsel = a.idx ? clampi(c_raw, 0, min(a.k_max, N)) : N;
+    const int L = nsel + a.nv;
+    const int p1 = min(p0 + a.spl, L);
+    const int cnt = max(p1 - p0, 0);
+    const int full_end = min(p1, nsel);   // positions below this need no mask
+    const int ntile = (cnt + kTile - 1) / kTile;
+
+    // ---- row offsets of the split's positions; the padding of the last step points at
+    //      token N (the first new token, always present), whose scores are masked ----
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < ntile * kTile) {
+            const int pos = p0 + i;
+            int tok;
+            if (i >= cnt)
+                tok = N;
+            else if (pos < nsel)
+                tok = a.idx ? clampi(raw[k], 0, N - 1) : pos;
+            else
+                tok = N + (pos - nsel);
+            sOffK[i] = row_offset(a.k, b, tok);
+            if (!a.kv_same)
+                sOffV[i] = row_offset(a.v, b, tok);
+        }
+    }
+    __syncthreads();                  // offset tables ready
+
+    f32x4 acc[G::DVT][QT];
+#pragma unroll
+    for (int i = 0; i < G::DVT; ++i)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
             acc[i][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float mref[QT], lrun[QT];         // reference max (log2 units) and running sum per query
+    float mref[QT], lrun[QT];         // reference max (scaled log2 units) and running sum
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         mref[qt] = -INFINITY;
         lrun[qt] = 0.f;
     }
 
-    const int ntile = (cnt + 15) >> 4;
-    const int mine = ntile > w ? (ntile - w + 3) >> 2 : 0;    // tiles w, w+4, ... of this wave
-    uint8_t *wring = lds + S::TAB + w * R * S::SLOT;           // this wave's ring of tile slots
+    const int mine = ntile > w ? (ntile - w + 3) >> 2 : 0;    // steps w, w+4, ... of this wave
+    uint8_t *wring = lds + S::TAB + w * R * G::SLOT;          // this wave's ring of step slots
+    const uint16_t *kbase = a.k.base + (int64_t)g * a.k.sh;
+    const uint16_t *vbase = a.v.base + (int64_t)g * a.v.sh;
+    const int dg = lane / G::CPR;     // DMA: row group of the lane within an instruction
+    const int dc = lane % G::CPR;     // DMA: LDS chunk of the lane within its row
 
-    // Tile jj of this wave into ring slot jj % R by LDS DMA: lane (quad, li) moves the
-    // quarter `quad` of row li of K and of V, 16 bytes per instruction (lane i's bytes
-    // land at slot + 16*i).  Issued for every step, also past the end (then it re-reads
-    // the split's last row into a slot nobody reads), so the waits count exactly.
+    // Step jj of this wave into ring slot jj % R: the lane moves rows dg*NI + n (n < NI)
+    // of the step, i.e. NI consecutive table entries.  Loads are non-temporal: every row
+    // is read once.
     auto dma = [&](int jj) {
-        const int rel = min(((w + 4 * jj) << 4) + li, cnt - 1);
-        const int tok = sTok[rel];
-        int64_t ko, vo;
-        if (a.k.pt)
-            ko = (int64_t)sPgK[rel] * a.k.sp + (int64_t)(tok & ((1 << a.k.ps_log2) - 1)) * a.k.st;
-        else
-            ko = (int64_t)b * a.k.sb + (int64_t)tok * a.k.st;
-        if (a.v.pt)
-            vo = (int64_t)sPgV[rel] * a.v.sp + (int64_t)(tok & ((1 << a.v.ps_log2) - 1)) * a.v.st;
-        else
-            vo = (int64_t)b * a.v.sb + (int64_t)tok * a.v.st;
-        const uint16_t *kp = a.k.base + ko + (int64_t)g * a.k.sh + quad * S::QD;
-        const uint16_t *vp = a.v.base + vo + (int64_t)g * a.v.sh + quad * S::QD;
-        uint8_t *slot = wring + (jj % R) * S::SLOT;
+        const int e0 = (w + 4 * jj) * kTile + dg * G::NI;
+        uint8_t *slot = wring + (jj % R) * G::SLOT;
 #pragma unroll
-        for (int i = 0; i < S::KS; ++i)
-            __builtin_amdgcn_global_load_lds(kp + i * 8, (lds_void *)(slot + i * 1024), 16, 0, 0);
+        for (int n = 0; n < G::NI; ++n) {
+            const int rho = n * G::RPI + dg;
+            const int ck = dc ^ (rho % G::CPR);
+            __builtin_amdgcn_global_load_lds(kbase + sOffK[e0 + n] + ck * 8, (lds_void *)(slot + n * 1024), 16, 0, 2);
+        }
 #pragma unroll
-        for (int i = 0; i < S::KS; ++i)
-            __builtin_amdgcn_global_load_lds(vp + i * 8, (lds_void *)(slot + (S::KS + i) * 1024), 16, 0, 0);
+        for (int n = 0; n < G::NI; ++n) {
+            const int rho = n * G::RPI + dg;
+            const int cv = dc ^ ((2 * rho) % G::CPR);
+            __builtin_amdgcn_global_load_lds(vbase + sOffV[e0 + n] + cv * 8,
+                                             (lds_void *)(slot + G::HALF + n * 1024), 16, 0, 2);
+        }
     };
 
-    if (mine > 0) {
+    // per-lane LDS byte offsets of the operand reads (slot-relative)
+    int koff[2][G::KS];               // K: row 16h + li, chunk ks*4 + quad
 #pragma unroll
-        for (int jj = 0; jj < R - 1; ++jj)
-            dma(jj);
-        for (int jj = 0; jj < mine; ++jj) {
-            dma(jj + R - 1);
-            wait_vmcnt<2 * S::KS * (R - 1)>();      // tile jj has landed; R-1 tiles stay in flight
-            __builtin_amdgcn_sched_barrier(0);
-            const uint8_t *slot = wring + (jj % R) * S::SLOT;
-            const int pos0 = p0 + ((w + 4 * jj) << 4);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+            const int rho = 16 * h + li;
+            koff[h][ks] = rho * G::RB + (((ks * 4 + quad) ^ (rho % G::CPR)) << 4);
+        }
+    // V^T: source lane s = li of group quad reads row 16h + 4*quad + s/4, head-dim
+    // columns dt*16 + 4*(s%4) .. +3, i.e. chunk 2*dt + (s%4)/2, byte 8*(s%2) of it
+    int vrow[2], vf2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int rho = 16 * h + 4 * quad + (li >> 2);
+        vrow[h] = G::HALF + rho * G::RB + (((li >> 1) & 1) << 4) + ((li & 1) << 3);
+        vf2[h] = rho % (G::CPR / 2);
+    }
+    // list row of the lane's S^T entries (h, r): LDS row 16h + 4*quad + r
+    int trow[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            trow[h][r] = G::tau(16 * h + 4 * quad + r);
 
-            // S^T = K Q^T: the lane's own K bytes are its A operand
-            u32x4 kop[S::KS];
+    if (mine > 0) {
+        // All R slots are in flight while a step computes: a slot is refilled as soon as
+        // its K and V operands have been read into registers, before the step's math.
+        dma(0);
+        load_q();
 #pragma unroll
-            for (int i = 0; i < S::KS; ++i)
-                kop[i] = *reinterpret_cast<const u32x4 *>(slot + i * 1024 + lane * 16);
-            f32x4 s[QT];
+        for (int jj = 1; jj < R; ++jj)
+            if (jj < mine)
+                dma(jj);
+        for (int jj = 0; jj < mine; ++jj) {
+            if (jj + R - 1 < mine)
+                wait_vmcnt<2 * G::NI * (R - 1)>();   // step jj has landed, R-1 later steps in flight
+            else
+                wait_vmcnt<0>();
+            __builtin_amdgcn_sched_barrier(0);
+            const uint8_t *slot = wring + (jj % R) * G::SLOT;
+            const int pos0 = p0 + (w + 4 * jj) * kTile;
+
+            u32x4 kop[2][G::KS];
 #pragma unroll
-            for (int qt = 0; qt < QT; ++qt) {
-                s[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int ks = 0; ks < S::KS; ++ks)
-                    s[qt] = mfma_bf16(kop[ks], qop[qt][ks], s[qt]);
+                for (int ks = 0; ks < G::KS; ++ks)
+                    kop[h][ks] = *reinterpret_cast<const u32x4 *>(slot + koff[h][ks]);
+            // V^T operands (16-bit transposing reads)
+            u32x4 vop[G::DVT];
+#pragma unroll
+            for (int dt = 0; dt < G::DVT; ++dt) {
+                const u32x2 v0 = lds_read_tr16(slot + vrow[0] + ((dt ^ vf2[0]) << 5));
+                const u32x2 v1 = lds_read_tr16(slot + vrow[1] + ((dt ^ vf2[1]) << 5));
+                vop[dt] = u32x4{v0[0], v0[1], v1[0], v1[1]};
             }
-            // lane holds tokens pos0 + 4*quad + r (r = 0..3) for query row qt*16 + li
-            const bool full = pos0 + 16 <= full_end;
-            u32x2 pb[QT];
+            if (jj + R < mine) {
+                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the slot's reads are done
+                __builtin_amdgcn_sched_barrier(0);
+                dma(jj + R);
+            }
+
+            // S^T = K Q^T for both 16-row halves of the step
+            f32x4 s[2][QT];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) {
+                    s[h][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < G::KS; ++ks)
+                        s[h][qt] = mfma_bf16(kop[h][ks], qop[qt][ks], s[h][qt]);
+                }
+
+            const bool full = pos0 + kTile <= full_end;
+            u32x4 pb[QT];
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) {
-                if (full) {
-                    s[qt] *= a.scale_log2;
-                } else {
+                if (!full) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int pos = pos0 + 4 * quad + r;
-                        const bool ok = (pos < p1) & ((pos < nsel) | (pos - nsel <= qrow_t[qt]));
-                        s[qt][r] = ok ? s[qt][r] * a.scale_log2 : -INFINITY;
-                    }
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int pos = pos0 + trow[h][r];
+                            const bool ok = (pos < p1) & ((pos < nsel) | (pos - nsel <= qrow_t[qt]));
+                            s[h][qt][r] = ok ? s[h][qt][r] : -INFINITY;
+                        }
                 }
-                float mx = fmaxf(fmaxf(s[qt][0], s[qt][1]), fmaxf(s[qt][2], s[qt][3]));
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                float mx = fmaxf(fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3])),
+                                 fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
+                mx = max_over_quads(mx) * c;
                 if (__any(mx > mref[qt] + kLazy)) {
                     const float mnew = fmaxf(mref[qt], mx);
                     const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref[qt] - mnew);
                     mref[qt] = mnew;
                     lrun[qt] *= alpha;
 #pragma unroll
-                    for (int i = 0; i < S::DVT; ++i)
+                    for (int i = 0; i < G::DVT; ++i)
                         acc[i][qt] *= alpha;
                 }
-                const float muse = mref[qt] == -INFINITY ? 0.f : mref[qt];
-                float p[4];
+                const float nm = mref[qt] == -INFINITY ? 0.f : -mref[qt];
+                float p[2][4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    p[r] = fast_exp2(s[qt][r] - muse);
-                lrun[qt] += (p[0] + p[1]) + (p[2] + p[3]);
-                pb[qt] = u32x2{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])};
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        p[h][r] = fast_exp2(fmaf(s[h][qt][r], c, nm));
+                lrun[qt] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+                pb[qt] = u32x4{cvt_pk_bf16(p[0][0], p[0][1]), cvt_pk_bf16(p[0][2], p[0][3]),
+                               cvt_pk_bf16(p[1][0], p[1][1]), cvt_pk_bf16(p[1][2], p[1][3])};
             }
-            // O^T += V^T P^T: V read transposed out of the DMA'd tile — column dv of rows
-            // 4*quad + j sits in DMA instruction (dv % QD) / 8 of lane group dv / QD
-            const uint8_t *vslot = slot + S::KS * 1024;
+            // O^T += V^T P^T over the 32 positions (16x16x32: k-slot (quad, 4h + r) is LDS
+            // row 16h + 4*quad + r in both operands)
 #pragma unroll
-            for (int dt = 0; dt < S::DVT; ++dt) {
-                const int dv = dt * 16 + li;
-                const int within = dv % S::QD;
-                const uint8_t *col = vslot + (within >> 3) * 1024 + ((dv / S::QD) * 16 + 4 * quad) * 16 + (within & 7) * 2;
-                const uint32_t e0 = *reinterpret_cast<const uint16_t *>(col);
-                const uint32_t e1 = *reinterpret_cast<const uint16_t *>(col + 16);
-                const uint32_t e2 = *reinterpret_cast<const uint16_t *>(col + 32);
-                const uint32_t e3 = *reinterpret_cast<const uint16_t *>(col + 48);
-                const u32x2 vop{e0 | (e1 << 16), e2 | (e3 << 16)};
+            for (int dt = 0; dt < G::DVT; ++dt)
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt)
-                    acc[dt][qt] = mfma_bf16_k16(vop, pb[qt], acc[dt][qt]);
-            }
+                    acc[dt][qt] = mfma_bf16(vop[dt], pb[qt], acc[dt][qt]);
         }
-        wait_vmcnt<0>();              // trailing DMAs done before the LDS is reused
     }
 
-    // ---- merge the four waves: row sums over lane groups, then waves 1..3 into wave 0 ----
+    // ---- merge the four waves in one LDS exchange: every wave publishes its maxima,
+    //      sums and O^T accumulators, then wave w merges head-dim tiles
+    //      [w*DVT/4, (w+1)*DVT/4) of every row and writes them ----
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         lrun[qt] += __shfl_xor(lrun[qt], 16);
         lrun[qt] += __shfl_xor(lrun[qt], 32);
     }
-    float *mAcc = reinterpret_cast<float *>(lds + S::TAB);
-    float *mM = mAcc + 64 * S::ACC;
-    float *mL = mM + S::QR;
-    for (int src = 1; src < 4; ++src) {
-        __syncthreads();              // ring / previous round no longer read
-        if (w == src) {
+    float *xAcc = reinterpret_cast<float *>(lds + S::TAB);   // [wave][dv tile][qt][lane][4]
+    float *xM = xAcc + 4 * 64 * S::ACC;                       // [wave][QR]
+    float *xL = xM + 4 * S::QR;
+    __syncthreads();                  // every wave is done with its ring
 #pragma unroll
-            for (int i = 0; i < S::DVT; ++i)
+    for (int i = 0; i < G::DVT; ++i)
 #pragma unroll
-                for (int qt = 0; qt < QT; ++qt)
-                    *reinterpret_cast<f32x4 *>(mAcc + ((i * QT + qt) * 64 + lane) * 4) = acc[i][qt];
-            if (quad == 0) {
-#pragma unroll
-                for (int qt = 0; qt < QT; ++qt) {
-                    mM[qt * 16 + li] = mref[qt];
-                    mL[qt * 16 + li] = lrun[qt];
-                }
-            }
-        }
-        __syncthreads();
-        if (w == 0) {
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) {
-                const float m2 = mM[qt * 16 + li];
-                const float M = fmaxf(mref[qt], m2);
-                const float f1 = M == -INFINITY ? 0.f : fast_exp2(mref[qt] - M);
-                const float f2 = M == -INFINITY ? 0.f : fast_exp2(m2 - M);
-                lrun[qt] = lrun[qt] * f1 + mL[qt * 16 + li] * f2;
-                mref[qt] = M;
-#pragma unroll
-                for (int i = 0; i < S::DVT; ++i)
-                    acc[i][qt] = acc[i][qt] * f1 +
-                                 *reinterpret_cast<const f32x4 *>(mAcc + ((i * QT + qt) * 64 + lane) * 4) * f2;
-            }
-        }
-    }
-    if (w != 0)
-        return;
-
-    if (a.splits == 1) {
-        // ---- final output straight from registers ----
+        for (int qt = 0; qt < QT; ++qt)
+            *reinterpret_cast<f32x4 *>(xAcc + (((w * G::DVT + i) * QT + qt) * 64 + lane) * 4) = acc[i][qt];
+    if (quad == 0) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-            const int row = qg * S::QR + qt * 16 + li;
-            if (row >= a.GV)
-                continue;
-            const int t = row / a.G;
-            const int h = g * a.G + (row - t * a.G);
-            const float inv = 1.f / lrun[qt];
-            uint16_t *o = a.out + ((int64_t)(b * a.nv + t) * a.Hq + h) * D;
-#pragma unroll
-            for (int i = 0; i < S::DVT; ++i) {
-                const int dv = i * 16 + 4 * quad;
-                *reinterpret_cast<u32x2 *>(o + dv) =
-                    u32x2{pack_bf16x2(acc[i][qt][0] * inv, acc[i][qt][1] * inv),
-                          pack_bf16x2(acc[i][qt][2] * inv, acc[i][qt][3] * inv)};
-            }
-            if (quad == 0)
-                a.lse[((int64_t)b * a.Hq + h) * a.nv + t] = (mref[qt] + __log2f(lrun[qt])) * kLn2;
+            xM[w * S::QR + qt * 16 + li] = mref[qt];
+            xL[w * S::QR + qt * 16 + li] = lrun[qt];
         }
-        return;
     }
+    __syncthreads();
 
-    // ---- split partial for the merge kernel: acc [QR][D], then m [QR], l [QR] ----
+    constexpr int DPW = G::DVT / 4;   // head-dim tiles merged by each wave
     const int64_t pstride = (int64_t)S::QR * D + 2 * S::QR;
     float *part = a.part + ((int64_t)pair * a.splits + split) * pstride;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         const int q = qt * 16 + li;
-        if (qg * S::QR + q >= a.GV)
-            continue;                 // padding rows are never merged
+        const int row = qg * S::QR + q;
+        if (row >= a.GV)
+            continue;                 // padding rows are never written
+        float mw[4], M = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < S::DVT; ++i)
-            *reinterpret_cast<f32x4 *>(part + (int64_t)q * D + i * 16 + 4 * quad) = acc[i][qt];
-        if (quad == 0) {
-            part[S::QR * D + q] = mref[qt];
-            part[S::QR * D + S::QR + q] = lrun[qt];
+        for (int v = 0; v < 4; ++v) {
+            mw[v] = xM[v * S::QR + q];
+            M = fmaxf(M, mw[v]);
+        }
+        float f[4], l = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            f[v] = M == -INFINITY ? 0.f : fast_exp2(mw[v] - M);
+            l += f[v] * xL[v * S::QR + q];
+        }
+        const int t = row / a.G;
+        const int h = g * a.G + (row - t * a.G);
+        const float inv = 1.f / l;
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+            const int i = w * DPW + j;
+            f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                o += f[v] * *reinterpret_cast<const f32x4 *>(xAcc + (((v * G::DVT + i) * QT + qt) * 64 + lane) * 4);
+            const int dv = i * 16 + 4 * quad;
+            if (a.splits == 1) {
+                uint16_t *op = a.out + ((int64_t)(b * a.nv + t) * a.Hq + h) * D + dv;
+                *reinterpret_cast<u32x2 *>(op) =
+                    u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+            } else {
+                *reinterpret_cast<f32x4 *>(part + (int64_t)q * D + dv) = o;
+            }
+        }
+        if (w == 0 && quad == 0) {
+            if (a.splits == 1) {
+                a.lse[((int64_t)b * a.Hq + h) * a.nv + t] = (M + __log2f(l)) * kLn2;
+            } else {
+                part[S::QR * D + q] = M;
+                part[S::QR * D + S::QR + q] = l;
+            }
         }
     }
 }
 
-// Merges the split partials of one (pair, 16-row query tile) in fixed split order:
+// Merges the split partials of one (pair, query tile) in fixed split order:
 // O = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s, LSE = M + log sum_s e^{m_s - M} l_s.
-// Every (row, 4-column) item is one thread; the per-split maxima and sums of a row are
-// read by all of its threads (cache hits), so there is a single round of loads.
+// Every (row, 4-column) item is one thread (D/64 blocks per 16-row tile); the per-split
+// maxima and sums of a row are read by all of its threads (cache hits), so there is a
+// single round of loads.
 template <int D, int QT>
 __global__ __launch_bounds__(kThreads) void verify_attn_merge_kernel(AttnArgs a)
 {
     constexpr int QR = QT * 16;
+    constexpr int BPQ = D / 64;       // blocks per 16-row query tile
     constexpr int kPre = 8;           // splits whose partials are fetched before any math
-    const int pair = blockIdx.x / QT;
-    const int qt = blockIdx.x - pair * QT;
-    const int qg = pair % a.qgroups;
-    const int bg = pair / a.qgroups;
+    // blocks of a pair run on the XCD that ran its split workgroups (blockIdx % 8)
+    const int x = blockIdx.x;
+    const int hi = x >> 3;
+    const int k = hi % (QT * BPQ);
+    const int t2 = hi / (QT * BPQ);
+    const int qg = t2 % a.qgroups;
+    const int bg = (t2 / a.qgroups) * 8 + (x & 7);
+    if (bg >= a.B * a.Hkv)
+        return;
+    const int pair = bg * a.qgroups + qg;
+    const int qt = k / BPQ;
     const int g = bg % a.Hkv;
     const int b = bg / a.Hkv;
-    const int row0 = qg * QR + qt * 16;
-    const int rows = min(16, a.GV - row0);
+    const int item = (k - qt * BPQ) * kThreads + threadIdx.x;
+    const int r = item / (D / 4);
+    const int dv = (item - r * (D / 4)) * 4;
+    const int row = qg * QR + qt * 16 + r;
+    if (row >= a.GV)
+        return;
+    const int q = qt * 16 + r;
     const int64_t pstride = (int64_t)QR * D + 2 * QR;
     const float *base = a.part + (int64_t)pair * a.splits * pstride;
-    for (int item = threadIdx.x; item < rows * (D / 4); item += kThreads) {
-        const int r = item / (D / 4);
-        const int dv = (item - r * (D / 4)) * 4;
-        const int q = qt * 16 + r;
-        float ms[kPre], ls[kPre];
-        f32x4 as[kPre];
+    float ms[kPre], ls[kPre];
+    f32x4 as[kPre];
 #pragma unroll
-        for (int sp = 0; sp < kPre; ++sp) {
-            if (sp < a.splits) {
-                const float *ps = base + sp * pstride;
-                ms[sp] = ps[QR * D + q];
-                ls[sp] = ps[QR * D + QR + q];
-                as[sp] = *reinterpret_cast<const f32x4 *>(ps + (int64_t)q * D + dv);
-            }
-        }
-        float M = -INFINITY;
-#pragma unroll
-        for (int sp = 0; sp < kPre; ++sp)
-            if (sp < a.splits)
-                M = fmaxf(M, ms[sp]);
-        for (int sp = kPre; sp < a.splits; ++sp)
-            M = fmaxf(M, base[sp * pstride + QR * D + q]);
-        f32x4 num{0.f, 0.f, 0.f, 0.f};
-        float den = 0.f;
-#pragma unroll
-        for (int sp = 0; sp < kPre; ++sp) {
-            if (sp < a.splits) {
-                const float wgt = fast_exp2(ms[sp] - M);
-                num += wgt * as[sp];
-                den += wgt * ls[sp];
-            }
-        }
-        for (int sp = kPre; sp < a.splits; ++sp) {
+    for (int sp = 0; sp < kPre; ++sp) {
+        if (sp < a.splits) {
             const float *ps = base + sp * pstride;
-            const float wgt = fast_exp2(ps[QR * D + q] - M);
-            num += wgt * *reinterpret_cast<const f32x4 *>(ps + (int64_t)q * D + dv);
-            den += wgt * ps[QR * D + QR + q];
+            ms[sp] = ps[QR * D + q];
+            ls[sp] = ps[QR * D + QR + q];
+            as[sp] = *reinterpret_cast<const f32x4 *>(ps + (int64_t)q * D + dv);
         }
-        const float inv = 1.f / den;
-        const int row = row0 + r;
-        const int t = row / a.G;
-        const int h = g * a.G + (row - t * a.G);
-        uint16_t *o = a.out + ((int64_t)(b * a.nv + t) * a.Hq + h) * D + dv;
-        *reinterpret_cast<u32x2 *>(o) =
-            u32x2{pack_bf16x2(num[0] * inv, num[1] * inv), pack_bf16x2(num[2] * inv, num[3] * inv)};
-        if (dv == 0)
-            a.lse[((int64_t)b * a.Hq + h) * a.nv + t] = (M + __log2f(den)) * kLn2;
     }
+    float M = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < kPre; ++sp)
+        if (sp < a.splits)
+            M = fmaxf(M, ms[sp]);
+    for (int sp = kPre; sp < a.splits; ++sp)
+        M = fmaxf(M, base[sp * pstride + QR * D + q]);
+    f32x4 num{0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < kPre; ++sp) {
+        if (sp < a.splits) {
+            const float wgt = M == -INFINITY ? 0.f : fast_exp2(ms[sp] - M);
+            num += wgt * as[sp];
+            den += wgt * ls[sp];
+        }
+    }
+    for (int sp = kPre; sp < a.splits; ++sp) {
+        const float *ps = base + sp * pstride;
+        const float wgt = M == -INFINITY ? 0.f : fast_exp2(ps[QR * D + q] - M);
+        num += wgt * *reinterpret_cast<const f32x4 *>(ps + (int64_t)q * D + dv);
+        den += wgt * ps[QR * D + QR + q];
+    }
+    const float inv = 1.f / den;
+    const int t = row / a.G;
+    const int h = g * a.G + (row - t * a.G);
+    uint16_t *o = a.out + ((int64_t)(b * a.nv + t) * a.Hq + h) * D + dv;
+    *reinterpret_cast<u32x2 *>(o) =
+        u32x2{pack_bf16x2(num[0] * inv, num[1] * inv), pack_bf16x2(num[2] * inv, num[3] * inv)};
+    if (dv == 0)
+        a.lse[((int64_t)b * a.Hq + h) * a.nv + t] = (M + __log2f(den)) * kLn2;
 }
 
 template <int D, int QT, int R>
@@ -444,7 +547,7 @@ hipError_t launch_qt(const AttnArgs &a, dim3 grid, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1)
         return e;
-    hipLaunchKernelGGL((verify_attn_merge_kernel<D, QT>), dim3((unsigned)(a.pairs * QT)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((verify_attn_merge_kernel<D, QT>), dim3((unsigned)((a.B * a.Hkv + 7) / 8 * 8 * a.qgroups * QT * (D / 64))), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -455,41 +558,58 @@ hipError_t launch_r(const AttnArgs &a, int qt, dim3 grid, hipStream_t st)
     case 1: return launch_qt<D, 1, R>(a, grid, st);
     case 2: return launch_qt<D, 2, R>(a, grid, st);
     case 3: return launch_qt<D, 3, R>(a, grid, st);
-    case 4: return launch_qt<D, 4, R>(a, grid, st);
-    default: return launch_qt<D, 5, R>(a, grid, st);
+    default: return launch_qt<D, 4, R>(a, grid, st);
     }
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs &a, int qt, int ring, dim3 grid, hipStream_t st)
 {
-    return ring >= 3 ? launch_r<D, 3>(a, qt, grid, st) : launch_r<D, 2>(a, qt, grid, st);
+    if constexpr (D == 64)
+        return ring >= 3 ? launch_r<D, 3>(a, qt, grid, st) : launch_r<D, 2>(a, qt, grid, st);
+    else
+        return launch_r<D, 2>(a, qt, grid, st);   // two 16 KB slots per wave fill the LDS
 }
 
 }  // namespace
 
-AttnPlan plan_attn(int B, int Hkv, int G, int nv, int max_list, int target_wgs)
+AttnPlan plan_attn(int B, int Hkv, int G, int nv, int max_list, int target_wgs, int split_cap)
 {
     AttnPlan p;
     const int gv = G * nv;
     const int qt_total = (gv + 15) / 16;
-    p.qgroups = (qt_total + kMaxQT - 1) / kMaxQT;
-    p.qt = (qt_total + p.qgroups - 1) / p.qgroups;
-    p.pairs = B * Hkv * p.qgroups;
+    const int base = B * Hkv;
     const int list = max(1, max_list);
-    int s = (target_wgs + p.pairs - 1) / max(1, p.pairs);
-    s = max(s, (list + kSplitMax - 1) / kSplitMax);        // the token table holds kSplitMax positions
-    s = max(1, min(min(s, (list + 15) / 16), kMaxSplits));
-    p.spl = ((list + s - 1) / s + 15) / 16 * 16;
+    const int target = max(1, target_wgs);
+    const int min_s = (list + split_cap - 1) / split_cap;   // the offset table holds split_cap positions
+    // Query-row groups only as needed for the register budget: every group streams the
+    // pair's K/V rows again.
+    const int qg = (qt_total + kMaxQT - 1) / kMaxQT;
+    p.qt = (qt_total + qg - 1) / qg;
+    p.qgroups = (qt_total + p.qt - 1) / p.qt;
+    p.pairs = base * p.qgroups;
+    // Token splits (merged by a second kernel): the minimum, unless the grid would leave
+    // more than half of a round idle; then rounded up to whole rounds.
+    int s = min_s;
+    if ((long)p.pairs * s * 2 <= target)
+        s = (target + p.pairs - 1) / p.pairs;
+    if ((long)p.pairs * s > target) {
+        const long rounds = ((long)p.pairs * s + target - 1) / target;
+        s = max(s, (int)(rounds * target / p.pairs));
+    }
+    const int max_s = min((list + kTile - 1) / kTile, kMaxSplits);
+    s = max(1, min(s, max_s));
+    s = max(s, min_s);
+    p.spl = ((list + s - 1) / s + kTile - 1) / kTile * kTile;
     p.splits = (list + p.spl - 1) / p.spl;
     p.part_floats = p.splits > 1 ? (size_t)p.pairs * p.splits * ((size_t)p.qt * 16 * 128 + 2 * p.qt * 16) : 0;
-    p.grid = (size_t)((p.pairs + 7) / 8) * 8 * p.splits;
+    p.grid = (size_t)((base + 7) / 8) * 8 * p.qgroups * p.splits;
     return p;
 }
 
 hipError_t launch_attn(const AttnArgs &a, int head_dim, int qt, int ring, hipStream_t st)
 {
-    const dim3 grid((unsigned)(((a.pairs + 7) / 8) * 8 * a.splits));
+    const dim3 grid((unsigned)(((a.B * a.Hkv + 7) / 8) * 8 * a.qgroups * a.splits));
     return head_dim == 64 ? launch_d<64>(a, qt, ring, grid, st) : launch_d<128>(a, qt, ring, grid, st);
 }
 

@@ -10,14 +10,17 @@
 namespace dustin {
 
 // ---------------------------------------------------------------- attention
-constexpr int kMaxQT = 5;        // 16-row query tiles held by one workgroup
-constexpr int kSplitMax = 1024;  // list positions of one workgroup (its LDS token table)
-constexpr int kMaxSplits = 128;  // splits of one (sequence, KV head, query group)
+constexpr int kMaxQT = 4;          // 16-row query tiles held by one workgroup
+constexpr int kSplitMax = 2080;    // list positions of one workgroup (65 steps of 32) when K and
+                                   // V rows share their offsets; half as many when they do not
+constexpr int kMaxSplits = 128;    // splits of one (sequence, KV head, query group)
+constexpr int kMaxList = 131072;   // longest list (selected positions + new tokens) accepted
 
 struct AttnArgs {
     int B, Hq, Hkv, G, nv, GV;
     const uint16_t *q;
     KvView k, v;
+    int kv_same;             // K and V rows of a token sit at the same element offsets
     const int32_t *ctx_len;
     const int32_t *idx;      // nullptr = dense: the list is [0, ctx_len[b])
     const int32_t *count;
@@ -27,7 +30,7 @@ struct AttnArgs {
     uint16_t *out;
     float *lse;
     float *part;             // split partials
-    int splits, spl, qgroups, pairs;   // spl: list positions per split
+    int splits, spl, qgroups, pairs;   // spl: list positions per split; pairs = B*Hkv*qgroups
 };
 
 struct AttnPlan {
@@ -36,7 +39,7 @@ struct AttnPlan {
     size_t grid;
 };
 
-AttnPlan plan_attn(int B, int Hkv, int G, int nv, int max_list, int target_wgs);
+AttnPlan plan_attn(int B, int Hkv, int G, int nv, int max_list, int target_wgs, int split_cap);
 hipError_t launch_attn(const AttnArgs &a, int head_dim, int qt, int ring, hipStream_t st);
 
 // ---------------------------------------------------------------- scoring
