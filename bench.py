@@ -10,8 +10,14 @@ cache by an earlier layer.
 One step = draft-SRH scoring + target-SRH scoring + selection + sparse verification
 attention over all 80 layers.  `value` is the step's algorithmic HBM bytes divided by
 the step time (GB/s); the step time itself is `step_us`.  The roofline entry is for the
-dominant kernel (verification attention): its algorithmic bytes per launch divided by
-its average launch duration, timed with HIP events on the stream it runs on.
+dominant call, the sparse verification attention of one layer (a split kernel and, when
+the list is split, a merge kernel): its algorithmic bytes per call divided by its average
+duration, timed with HIP events on the stream it runs on.  `traffic` is the measured
+HBM bytes per call (FETCH_SIZE + WRITE_SIZE counters, calibrated on a copy of known
+size) from the committed counter summary, and null when the kernel source has changed
+since those counters were taken.
+
+`--counters` runs only a calibration copy and the attention calls, for counter passes.
 """
 from __future__ import annotations
 
@@ -27,6 +33,33 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse-verify step µs + achieved HBM GB/s (B=8, 32k ctx, budget 2048, γ=4)"
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "verify_attn_qwen72b_b8_n32768_traffic.md")
+ATTN_SOURCES = [os.path.join(ROOT, "sparse_kv_attention_amd", "csrc", f) for f in ("attn.hip", "launch.hpp", "device.hpp")]
+CALIB_BYTES = 256 << 20
+
+
+def attn_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per attention call from the committed counter summary, if it was taken
+    on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if line.startswith("traffic-json: "):
+                    d = json.loads(line[len("traffic-json: "):])
+                    if d.get("source_sha256_16") == attn_source_hash():
+                        return d["bytes_per_call"]
+    except OSError:
+        pass
+    return None
 
 
 def attn_bytes(B, Hq, Hkv, d, nv, counts):
@@ -54,6 +87,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--dense-layers", type=int, default=8)
+    ap.add_argument("--counters", action="store_true", help="calibration copy + attention calls only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -79,6 +113,22 @@ def main():
     T = w.target
     B, nv = w.batch, w.n_verify
     stream = torch.cuda.current_stream()
+
+    if args.counters:
+        # a plain copy of CALIB_BYTES (read CALIB_BYTES, write CALIB_BYTES), then ten
+        # distinct-layer attention calls
+        src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        step.score()
+        step.select()
+        for l in step.layers[:10]:
+            step.attn(l)
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": True, "calib_bytes": CALIB_BYTES, "attn_calls": 10,
+                          "attn_source_sha256_16": attn_source_hash()}), flush=True)
+        return
 
     # ---- warmup ----
     for _ in range(args.warmup):
@@ -138,7 +188,8 @@ def main():
     b_step = b_score + b_select + len(attn_layers) * b_attn
     b_dense = attn_bytes(B, T.hq, T.hkv, T.d, nv, [n_ctx] * B) - B * n_ctx * 4   # no index list
     gbs = b_step / (step_ms * 1e-3) / 1e9
-    attn_gbs = b_attn / (us_attn_launch * 1e-6) / 1e9
+    us_attn_call = us_attn_all / len(attn_layers)     # back-to-back calls, events around the loop
+    attn_gbs = b_attn / (us_attn_call * 1e-6) / 1e9
 
     line = {
         "metric": METRIC,
@@ -159,16 +210,19 @@ def main():
                    "srh_streams": {"draft": len(inp.draft_groups), "target": len(inp.target_groups)}},
         "step_us": round(step_ms * 1e3, 1),
         "stages_us": {"score_both_signals": round(us_score, 2), "select": round(us_select, 2),
-                      "attn_per_launch": round(us_attn_launch, 2), "attn_all_layers": round(us_attn_all, 1)},
+                      "attn_per_call": round(us_attn_call, 2), "attn_per_call_own_events": round(us_attn_launch, 2),
+                      "attn_all_layers": round(us_attn_all, 1)},
         "bytes": {"step": b_step, "attn_per_launch": b_attn, "score": b_score, "select": b_select},
         "score_gbs": round(b_score / (us_score * 1e-6) / 1e9, 1),
         "dense_attn_per_layer_us": round(us_dense_layer, 2),
         "dense_attn_gbs": round(b_dense / (us_dense_layer * 1e-6) / 1e9, 1),
-        "attn_speedup_vs_dense": round(us_dense_layer / us_attn_launch, 2),
+        "attn_speedup_vs_dense": round(us_dense_layer / us_attn_call, 2),
         "wall_s_timed": round(wall, 3),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "verify_attn_kernel<128,3> (sparse verification attention, one layer)"},
+                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "kernel": "dustin_sparse_verify_attn, one layer: verify_attn_split_kernel<128,3,2> "
+                               "+ verify_attn_merge_kernel<128,3>",
+                     "algorithmic_bytes_per_call": b_attn, "call_us": round(us_attn_call, 2)},
     }
 
     if not args.no_cpu_baseline:
