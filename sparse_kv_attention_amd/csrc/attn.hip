@@ -158,7 +158,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
     for (int k = 0; k < PT; ++k) {
         const int i = tid + k * kThreads;
         const int pos = p0 + i;
-        raw[k] = (a.idx && i < a.spl && pos < a.k_max) ? a.idx[(int64_t)b * a.k_max + pos] : 0;
+        raw[k] = (a.idx && i < a.spl + a.nv && pos < a.k_max) ? a.idx[(int64_t)b * a.k_max + pos] : 0;
     }
     const int n_raw = a.ctx_len[b];
     const int c_raw = a.idx ? a.count[b] : 0;
@@ -196,7 +196,9 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
     const int N = clampi(n_raw, 0, a.ctx_clamp);
     const int nsel = a.idx ? clampi(c_raw, 0, min(a.k_max, N)) : N;
     const int L = nsel + a.nv;
-    const int p1 = min(p0 + a.spl, L);
+    // split ranges are sized on the selected positions; the last split also takes the
+    // new-token block (at most nv positions beyond its size)
+    const int p1 = split == a.splits - 1 ? L : min(p0 + a.spl, L);
     const int cnt = max(p1 - p0, 0);
     const int full_end = min(p1, nsel);   // positions below this need no mask
     const int ntile = (cnt + kTile - 1) / kTile;
@@ -579,17 +581,19 @@ AttnPlan plan_attn(int B, int Hkv, int G, int nv, int max_list, int target_wgs, 
     const int gv = G * nv;
     const int qt_total = (gv + 15) / 16;
     const int base = B * Hkv;
-    const int list = max(1, max_list);
+    // Splits are sized on the selected positions (the whole context when dense); the last
+    // split also takes the new-token block, so a split holds at most split_cap - 32.
+    const int sel = max(1, max_list - nv);
     const int target = max(1, target_wgs);
-    const int min_s = (list + split_cap - 1) / split_cap;   // the offset table holds split_cap positions
+    const int min_s = (sel + split_cap - 32 - 1) / (split_cap - 32);
     // Query-row groups only as needed for the register budget: every group streams the
     // pair's K/V rows again.
     const int qg = (qt_total + kMaxQT - 1) / kMaxQT;
     p.qt = (qt_total + qg - 1) / qg;
     p.qgroups = (qt_total + p.qt - 1) / p.qt;
     p.pairs = base * p.qgroups;
-    // Token splits (merged by a second kernel): the minimum, unless the grid would leave
-    // more than half of a round idle; then rounded up to whole rounds.
+    // Token splits: the minimum, unless the grid would leave more than half of a round
+    // idle; then rounded up to whole rounds.
     int s = min_s;
     if ((long)p.pairs * s * 2 <= target)
         s = (target + p.pairs - 1) / p.pairs;
@@ -597,11 +601,11 @@ AttnPlan plan_attn(int B, int Hkv, int G, int nv, int max_list, int target_wgs, 
         const long rounds = ((long)p.pairs * s + target - 1) / target;
         s = max(s, (int)(rounds * target / p.pairs));
     }
-    const int max_s = min((list + kTile - 1) / kTile, kMaxSplits);
+    const int max_s = min((sel + kTile - 1) / kTile, kMaxSplits);
     s = max(1, min(s, max_s));
     s = max(s, min_s);
-    p.spl = ((list + s - 1) / s + kTile - 1) / kTile * kTile;
-    p.splits = (list + p.spl - 1) / p.spl;
+    p.spl = ((sel + s - 1) / s + kTile - 1) / kTile * kTile;
+    p.splits = (sel + p.spl - 1) / p.spl;
     p.part_floats = p.splits > 1 ? (size_t)p.pairs * p.splits * ((size_t)p.qt * 16 * 128 + 2 * p.qt * 16) : 0;
     p.grid = (size_t)((base + 7) / 8) * 8 * p.qgroups * p.splits;
     return p;
