@@ -39,21 +39,12 @@ constexpr float kLazy = 8.f;       // rescale O only when a tile's max exceeds t
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32)
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
 {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2_t));
-}
-
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // max over the four lanes l, l^16, l^32, l^48 (v_permlane32_swap / v_permlane16_swap)
@@ -254,14 +245,14 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
         for (int n = 0; n < G::NI; ++n) {
             const int rho = n * G::RPI + dg;
             const int ck = dc ^ (rho % G::CPR);
-            __builtin_amdgcn_global_load_lds(kbase + sOffK[e0 + n] + ck * 8, (lds_void *)(slot + n * 1024), 16, 0, 2);
+            __builtin_amdgcn_global_load_lds(kbase + sOffK[e0 + n] + ck * 8, (lds_void *)(slot + n * 1024), 16, 0, kLoadNonTemporal);
         }
 #pragma unroll
         for (int n = 0; n < G::NI; ++n) {
             const int rho = n * G::RPI + dg;
             const int cv = dc ^ ((2 * rho) % G::CPR);
             __builtin_amdgcn_global_load_lds(vbase + sOffV[e0 + n] + cv * 8,
-                                             (lds_void *)(slot + G::HALF + n * 1024), 16, 0, 2);
+                                             (lds_void *)(slot + G::HALF + n * 1024), 16, 0, kLoadNonTemporal);
         }
     };
 
@@ -324,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
                 vop[dt] = u32x4{v0[0], v0[1], v1[0], v1[1]};
             }
             if (jj + R < mine) {
-                __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the slot's reads are done
+                wait_lgkm0();                        // the slot's reads are done
                 __builtin_amdgcn_sched_barrier(0);
                 dma(jj + R);
             }

@@ -97,4 +97,19 @@ __device__ __forceinline__ u32x4 load16(const uint16_t *p)
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// ---- LDS DMA (global_load_lds_dwordx4): lane i's 16 bytes land at lds + 16*i ---------
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kLoadNonTemporal = 2;   // cache-policy bit of the LDS DMA: rows read once
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// s_waitcnt lgkmcnt(0): every LDS access of the wave has completed
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
 }  // namespace dustin

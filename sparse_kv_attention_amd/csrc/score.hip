@@ -13,9 +13,10 @@
 //                    maximum — the ones that carry probability mass — keep full relative
 //                    precision even when logits are large; the tile leaves (max, sum of
 //                    exp2) per pair.
-//   srh_finalize     one workgroup per (1024 tokens, sequence): per pair, the global max
-//                    and 1/Z from the tile partials (fixed order, fp64), then per token
-//                    the sum over pairs of exp2(offset + tile max - max) / Z.
+//   srh_finalize     one workgroup per (1024 tokens, sequence): per pair (one wave per
+//                    pair, lanes over tiles) the global max and 1/Z from the tile
+//                    partials, then per token the sum over pairs of
+//                    exp2(offset + tile max - max) / Z.
 // Logit-sum mode (LOGIT_SUM2): srh_logit_sum computes the raw scaled logits on MFMA (bf16
 // in, fp32 accumulate; the sum's tolerance scales with the sum of |logits|), and the
 // finalize kernel sums them per token.
@@ -273,21 +274,29 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
     const bool prob = a.mode == DUSTIN_SCORE_PROB_SUM;
     const int tile0 = blockIdx.x * kFinTiles;
     if (prob) {
-        for (int p = tid; p < a.total_pairs; p += kThreads) {
+        // one wave per pair: lanes take the tiles; the max (fp64) and the normaliser (fp32
+        // exp2 of the fp64 difference, summed in fp64) are reduced across the wave
+        const int w = tid >> 6, lane = tid & 63;
+        for (int p = w; p < a.total_pairs; p += kThreads / 64) {
             const double *mx = a.tile_max + ((int64_t)b * a.total_pairs + p) * a.n_tiles;
             const float *sm = a.tile_sum + ((int64_t)b * a.total_pairs + p) * a.n_tiles;
             double M = -INFINITY;
-            for (int t = 0; t < a.n_tiles; ++t)
+            for (int t = lane; t < a.n_tiles; t += 64)
                 M = fmax(M, mx[t]);
+            M = wave_max_f64(M);
             double Z = 0.0;
-            for (int t = 0; t < a.n_tiles; ++t)
+            for (int t = lane; t < a.n_tiles; t += 64)
                 if (sm[t] > 0.f)
-                    Z += (double)sm[t] * exp2(mx[t] - M);
-            sInvZ[p] = Z > 0.0 ? (float)(1.0 / Z) : 0.f;
+                    Z += (double)sm[t] * (double)fast_exp2((float)(mx[t] - M));
 #pragma unroll
-            for (int t = 0; t < kFinTiles; ++t)
-                sOff[p][t] = tile0 + t < a.n_tiles && mx[tile0 + t] > -INFINITY
-                                 ? (float)(mx[tile0 + t] - M) : 0.f;
+            for (int o = 32; o > 0; o >>= 1)
+                Z += __shfl_xor(Z, o);
+            if (lane == 0)
+                sInvZ[p] = Z > 0.0 ? (float)(1.0 / Z) : 0.f;
+            if (lane < kFinTiles) {
+                const int t = tile0 + lane;
+                sOff[p][lane] = t < a.n_tiles && mx[t] > -INFINITY ? (float)(mx[t] - M) : 0.f;
+            }
         }
         __syncthreads();
     }
