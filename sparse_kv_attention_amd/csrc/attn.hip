@@ -100,16 +100,6 @@ struct AttnShape {
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// Element offset of token t's row (head 0) in a view; t lies in [0, cap).
-__device__ __forceinline__ int64_t row_offset(const KvView &v, int b, int t)
-{
-    if (v.pt) {
-        const int pg = clampi(v.pt[(int64_t)b * v.max_pages + (t >> v.ps_log2)], 0, v.num_pages - 1);
-        return (int64_t)pg * v.sp + (int64_t)(t & ((1 << v.ps_log2) - 1)) * v.st;
-    }
-    return (int64_t)b * v.sb + (int64_t)t * v.st;
-}
-
 template <int D, int QT, int R>
 __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
 {
@@ -195,22 +185,41 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
     const int ntile = (cnt + kTile - 1) / kTile;
 
     // ---- row offsets of the split's positions; the padding of the last step points at
-    //      token N (the first new token, always present), whose scores are masked ----
+    //      token N (the first new token, always present), whose scores are masked.  Paged
+    //      caches: every entry's page is fetched before any is used (one round trip) ----
+    int tokv[PT];
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        const int i = tid + k * kThreads;
+        const int pos = p0 + i;
+        int tok = N;
+        if (i < cnt)
+            tok = pos < nsel ? (a.idx ? clampi(raw[k], 0, N - 1) : pos) : N + (pos - nsel);
+        tokv[k] = tok;
+    }
+    int pgK[PT], pgV[PT];
+    if (a.k.pt) {
+#pragma unroll
+        for (int k = 0; k < PT; ++k)
+            pgK[k] = a.k.pt[(int64_t)b * a.k.max_pages + (tokv[k] >> a.k.ps_log2)];
+    }
+    if (a.v.pt && !a.kv_same) {
+#pragma unroll
+        for (int k = 0; k < PT; ++k)
+            pgV[k] = a.v.pt[(int64_t)b * a.v.max_pages + (tokv[k] >> a.v.ps_log2)];
+    }
 #pragma unroll
     for (int k = 0; k < PT; ++k) {
         const int i = tid + k * kThreads;
         if (i < ntile * kTile) {
-            const int pos = p0 + i;
-            int tok;
-            if (i >= cnt)
-                tok = N;
-            else if (pos < nsel)
-                tok = a.idx ? clampi(raw[k], 0, N - 1) : pos;
-            else
-                tok = N + (pos - nsel);
-            sOffK[i] = row_offset(a.k, b, tok);
+            const int tok = tokv[k];
+            sOffK[i] = a.k.pt ? (int64_t)clampi(pgK[k], 0, a.k.num_pages - 1) * a.k.sp +
+                                    (int64_t)(tok & ((1 << a.k.ps_log2) - 1)) * a.k.st
+                              : (int64_t)b * a.k.sb + (int64_t)tok * a.k.st;
             if (!a.kv_same)
-                sOffV[i] = row_offset(a.v, b, tok);
+                sOffV[i] = a.v.pt ? (int64_t)clampi(pgV[k], 0, a.v.num_pages - 1) * a.v.sp +
+                                        (int64_t)(tok & ((1 << a.v.ps_log2) - 1)) * a.v.st
+                                  : (int64_t)b * a.v.sb + (int64_t)tok * a.v.st;
         }
     }
     __syncthreads();                  // offset tables ready
@@ -489,33 +498,30 @@ __global__ __launch_bounds__(kThreads) void verify_attn_merge_kernel(AttnArgs a)
     const int q = qt * 16 + r;
     const int64_t pstride = (int64_t)QR * D + 2 * QR;
     const float *base = a.part + (int64_t)pair * a.splits * pstride;
+    // the first kPre splits' partials are loaded unconditionally (split index clamped, the
+    // copies weighted 0), so all their loads are in flight together
     float ms[kPre], ls[kPre];
     f32x4 as[kPre];
 #pragma unroll
     for (int sp = 0; sp < kPre; ++sp) {
-        if (sp < a.splits) {
-            const float *ps = base + sp * pstride;
-            ms[sp] = ps[QR * D + q];
-            ls[sp] = ps[QR * D + QR + q];
-            as[sp] = *reinterpret_cast<const f32x4 *>(ps + (int64_t)q * D + dv);
-        }
+        const float *ps = base + min(sp, a.splits - 1) * pstride;
+        ms[sp] = ps[QR * D + q];
+        ls[sp] = ps[QR * D + QR + q];
+        as[sp] = *reinterpret_cast<const f32x4 *>(ps + (int64_t)q * D + dv);
     }
     float M = -INFINITY;
 #pragma unroll
     for (int sp = 0; sp < kPre; ++sp)
-        if (sp < a.splits)
-            M = fmaxf(M, ms[sp]);
+        M = fmaxf(M, sp < a.splits ? ms[sp] : -INFINITY);
     for (int sp = kPre; sp < a.splits; ++sp)
         M = fmaxf(M, base[sp * pstride + QR * D + q]);
     f32x4 num{0.f, 0.f, 0.f, 0.f};
     float den = 0.f;
 #pragma unroll
     for (int sp = 0; sp < kPre; ++sp) {
-        if (sp < a.splits) {
-            const float wgt = M == -INFINITY ? 0.f : fast_exp2(ms[sp] - M);
-            num += wgt * as[sp];
-            den += wgt * ls[sp];
-        }
+        const float wgt = (sp < a.splits && M != -INFINITY) ? fast_exp2(ms[sp] - M) : 0.f;
+        num += wgt * as[sp];
+        den += wgt * ls[sp];
     }
     for (int sp = kPre; sp < a.splits; ++sp) {
         const float *ps = base + sp * pstride;
