@@ -181,3 +181,44 @@ def test_logit_sum2_pure_topk():
     w = W.shrink(w, srh_target=((0, 0), (0, 1), (0, 4), (0, 8)))
     inp = W.make_inputs(w, device="cuda")
     check_pipeline(inp, [0], [], [0, 1, 2], logit_sum2=True)
+
+
+def _paged_copy(x: torch.Tensor, page_size: int, seed: int):
+    """x [B][n][Hkv][d] into pages [B*npg][page_size][Hkv][d] under a random page table."""
+    B, n, H, d = x.shape
+    npg = (n + page_size - 1) // page_size
+    gen = torch.Generator().manual_seed(seed)
+    pt = torch.randperm(B * npg, generator=gen).to(torch.int32).view(B, npg).to(x.device)
+    padded = torch.zeros((B, npg * page_size, H, d), dtype=x.dtype, device=x.device)
+    padded[:, :n] = x
+    pages = torch.zeros((B * npg, page_size, H, d), dtype=x.dtype, device=x.device)
+    pages[pt.reshape(-1).long()] = padded.view(B * npg, page_size, H, d)
+    return pages, pt
+
+
+def test_k_and_v_at_different_row_offsets():
+    """K and V views whose rows sit at different offsets (V stored head-major; then K and V
+    paged under different page tables): the kernel resolves K and V rows separately."""
+    from sparse_kv_attention_amd import dustin as D
+    w = small("kv_layouts", 3, 1500, 16, 2, 128, 4, 400, 4, 32, 100, seed=19)
+    inp = W.make_inputs(w, device="cuda")
+    step = check_pipeline(inp, [0], [], [0, 1, 2])
+    bs = [0, 1, 2]
+    idx, cnt = step.idx.cpu().numpy(), step.count.cpu().numpy()
+    ref = oracle_attn(inp, 0, idx, cnt, bs)
+    refd = oracle_attn(inp, 0, None, None, bs, dense=True)
+    K, V = inp.k_cache[0], inp.v_cache[0]
+    v_head_major = torch.empty((V.shape[0], V.shape[2], V.shape[1], V.shape[3]), dtype=V.dtype,
+                               device=V.device).permute(0, 2, 1, 3)
+    v_head_major.copy_(V)
+    kp, ptk = _paged_copy(K, 16, 1)
+    vp, ptv = _paged_copy(V, 16, 2)
+    for name, kv in (("V head-major", (D.kv_view(K), D.kv_view(v_head_major))),
+                     ("K and V paged, different page tables", (D.kv_view(kp, ptk), D.kv_view(vp, ptv)))):
+        step.kv[0] = kv
+        step.attn(0)
+        torch.cuda.synchronize()
+        check_attn(step.out, step.lse, ref, bs, f"sparse, {name}")
+        step.dense(0)
+        torch.cuda.synchronize()
+        check_attn(step.out, step.lse, refd, bs, f"dense, {name}")
