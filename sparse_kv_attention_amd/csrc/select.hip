@@ -68,51 +68,91 @@ __device__ int block_scan(int v, int &total, int *sScan)
 }
 
 struct SelShared {
-    uint32_t hist[kCopies * kHistStride];
+    uint32_t hist[2][kCopies * kHistStride];   // alternating: one is counted, the other cleared
     int scan[kWaves + 1];
     int bcast[2];
 };
 
 // Threshold of the `kth` largest eligible key (1 <= kth <= #eligible): returns the
 // threshold key and, in `need`, how many keys equal to it belong to the top kth.
+// Per 8-bit pass: every thread counts its keys into the current histogram (lane-slot
+// copies, one atomic per run of equal digits), one barrier, then wave 0 alone sums the copies, scans the bins from the top
+// with shuffles and picks the digit while the other waves clear the other histogram for
+// the next pass; one more barrier publishes the digit.  hist[0] must be zero on entry and
+// is zero again on return (the last pass counts into hist[1], which the next call's
+// first pass clears).
 template <int E>
 __device__ uint32_t radix_select(const uint32_t (&key)[E], uint64_t elig, int kth, int &need,
                                  SelShared &sh)
 {
     const int tid = threadIdx.x;
-    const int slot = (tid & 63) % kCopies;
+    const int lane = tid & 63;
+    const int slot = lane % kCopies;
     uint32_t prefix = 0;
     need = kth;
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        for (int i = tid; i < kCopies * kHistStride; i += kSelectThreads)
-            sh.hist[i] = 0;
-        __syncthreads();
+        uint32_t *hist = sh.hist[pass & 1];
+        uint32_t *other = sh.hist[(pass + 1) & 1];
+        // The thread's keys are consecutive positions, and in the early passes most of them
+        // share a digit: runs of equal digits are counted in a register and added with one
+        // atomic per run (keys that do not take part leave the current run open).
+        int cur = -1;
+        uint32_t run = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const bool match = pass == 0 || (key[e] >> (shift + 8)) == (prefix >> (shift + 8));
-            if (((elig >> e) & 1) && match)
-                atomicAdd(&sh.hist[slot * kHistStride + ((key[e] >> shift) & 255)], 1u);
+            if (((elig >> e) & 1) && match) {
+                const int d = (key[e] >> shift) & 255;
+                if (d != cur) {
+                    if (run)
+                        atomicAdd(&hist[slot * kHistStride + cur], run);
+                    cur = d;
+                    run = 0;
+                }
+                ++run;
+            }
         }
+        if (run)
+            atomicAdd(&hist[slot * kHistStride + cur], run);
         __syncthreads();
-        // suffix counts from the top bin down: thread t < 256 holds bin 255 - t
-        int cnt = 0;
-        if (tid < 256) {
-            const int bin = 255 - tid;
-            for (int c = 0; c < kCopies; ++c)
-                cnt += (int)sh.hist[c * kHistStride + bin];
-        }
-        int total;
-        const int before = block_scan(cnt, total, sh.scan);
-        if (tid < 256 && before < need && before + cnt >= need) {
-            sh.bcast[0] = 255 - tid;
-            sh.bcast[1] = need - before;
+        if (tid < 64) {
+            // lane holds bins 255-4l .. 252-4l (descending)
+            int c[4], tot = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int bin = 255 - 4 * lane - j;
+                int v = 0;
+#pragma unroll 8
+                for (int cp = 0; cp < kCopies; ++cp)
+                    v += (int)hist[cp * kHistStride + bin];
+                c[j] = v;
+                tot += v;
+            }
+            int incl = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o);
+                if (lane >= o)
+                    incl += y;
+            }
+            int before = incl - tot;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (before < need && before + c[j] >= need) {
+                    sh.bcast[0] = 255 - 4 * lane - j;
+                    sh.bcast[1] = need - before;
+                }
+                before += c[j];
+            }
+        } else {
+            for (int i = tid - 64; i < kCopies * kHistStride; i += kSelectThreads - 64)
+                other[i] = 0;
         }
         __syncthreads();
         prefix |= (uint32_t)sh.bcast[0] << shift;
         need = sh.bcast[1];
-        __syncthreads();
     }
     return prefix;
 }
@@ -126,25 +166,50 @@ __device__ uint64_t take_top(const uint32_t (&key)[E], uint64_t elig, int kth, S
     uint64_t sel = 0;
     int eq = 0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        if ((elig >> e) & 1) {
-            if (key[e] > thr)
-                sel |= 1ull << e;
-            else if (key[e] == thr)
-                ++eq;
-        }
+    for (int e = 0; e < E; ++e) {   // branch-free
+        const bool el = (elig >> e) & 1;
+        sel |= (uint64_t)(el && key[e] > thr) << e;
+        eq += (el && key[e] == thr) ? 1 : 0;
     }
     int total;
     int before = block_scan(eq, total, sh.scan);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        if (((elig >> e) & 1) && key[e] == thr) {
-            if (before < need)
-                sel |= 1ull << e;
-            ++before;
-        }
+        const bool tie = ((elig >> e) & 1) && key[e] == thr;
+        sel |= (uint64_t)(tie && before < need) << e;
+        before += tie ? 1 : 0;
     }
     return sel;
+}
+
+// The thread's E keys (positions base .. base+E-1 of one score row), masked by `valid`:
+// 16-byte loads when the row is 16-byte aligned and the range lies inside it, else
+// scalar loads at clamped positions.
+template <int E>
+__device__ __forceinline__ void load_keys(uint32_t (&key)[E], const float *row, int base, int n_max,
+                                          uint64_t valid)
+{
+    if ((n_max & 3) == 0 && base + E <= n_max) {
+        const float4 *p = reinterpret_cast<const float4 *>(row + base);
+        float4 v[E / 4];
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i)
+            v[i] = p[i];
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i) {
+            key[4 * i] = ord_key(v[i].x);
+            key[4 * i + 1] = ord_key(v[i].y);
+            key[4 * i + 2] = ord_key(v[i].z);
+            key[4 * i + 3] = ord_key(v[i].w);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            key[e] = ord_key(row[min(base + e, n_max - 1)]);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        key[e] = ((valid >> e) & 1) ? key[e] : 0u;
 }
 
 template <int E>
@@ -179,20 +244,17 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
                 prot |= 1ull << e;
         }
     }
+    for (int i = tid; i < kCopies * kHistStride; i += kSelectThreads)
+        sh.hist[0][i] = 0;
+    __syncthreads();
     uint32_t key[E];
     uint64_t selD = 0, selT = 0;
     if (md > 0) {
-        const float *sd = a.score_draft + (int64_t)b * a.n_max;
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            key[e] = ((valid >> e) & 1) ? ord_key(sd[base + e]) : 0u;
+        load_keys<E>(key, a.score_draft + (int64_t)b * a.n_max, base, a.n_max, valid);
         selD = take_top<E>(key, valid & ~prot, md, sh);
     }
     if (r > 0) {
-        const float *st = a.score_target + (int64_t)b * a.n_max;
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-            key[e] = ((valid >> e) & 1) ? ord_key(st[base + e]) : 0u;
+        load_keys<E>(key, a.score_target + (int64_t)b * a.n_max, base, a.n_max, valid);
         selT = take_top<E>(key, valid & ~prot & ~selD, r, sh);
     }
     const uint64_t fin = prot | selD | selT;
