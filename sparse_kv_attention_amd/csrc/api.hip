@@ -186,8 +186,8 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
 }
 
 struct ScoreWs {
-    int n_pad, n_tiles, total_pairs;
-    size_t logits_off, max_off, sum_off, bytes;
+    int n_pad, n_tiles, n_parts, total_pairs;
+    size_t logits_off, max_off, pmax_off, psum_off, bytes;
 };
 
 int pairs_per_qhead(int n_q, int mode) { return mode == DUSTIN_SCORE_PROB_SUM ? n_q : std::min(2, n_q); }
@@ -196,13 +196,19 @@ ScoreWs score_workspace(int B, int n_max, int total_qheads, int n_q, int mode)
 {
     ScoreWs w;
     w.n_pad = (n_max + 3) / 4 * 4;
-    w.n_tiles = std::max(1, (n_max + kProbTile - 1) / kProbTile);
+    w.n_tiles = std::max(1, (n_max + kStatTile - 1) / kStatTile);
+    // room for up to kScoreParts workgroup partials per pair; the launch picks how many
+    const int n_ld = std::max(1, (n_max + kProbTile - 1) / kProbTile);
+    w.n_parts = std::min(kScoreParts, n_ld);
     w.total_pairs = total_qheads * pairs_per_qhead(n_q, mode);
-    const size_t stats = mode == DUSTIN_SCORE_PROB_SUM ? (size_t)B * w.total_pairs * w.n_tiles : 0;
+    const bool prob = mode == DUSTIN_SCORE_PROB_SUM;
+    const size_t stats = prob ? (size_t)B * w.total_pairs * w.n_tiles : 0;
+    const size_t parts = prob ? (size_t)B * w.total_pairs * w.n_parts : 0;
     w.logits_off = 0;
     w.max_off = align_up(sizeof(float) * (size_t)B * w.total_pairs * w.n_pad);
-    w.sum_off = w.max_off + align_up(sizeof(double) * stats);
-    w.bytes = w.sum_off + align_up(sizeof(float) * stats);
+    w.pmax_off = w.max_off + align_up(sizeof(double) * stats);
+    w.psum_off = w.pmax_off + align_up(sizeof(double) * parts);
+    w.bytes = w.psum_off + align_up(sizeof(double) * parts);
     return w;
 }
 
@@ -275,13 +281,17 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
     a.total_qheads = total_qheads;
     a.total_pairs = lay.total_pairs;
     a.n_tiles = lay.n_tiles;
+    // softmax-mode logit kernel: two resident workgroups per CU (its LDS and register use),
+    // each streaming a run of tiles, so the grid is one round
+    a.n_parts = std::max(1, std::min(lay.n_parts, (2 * device_cus() + n_groups * B - 1) / (n_groups * B)));
     a.ctx_clamp = ctx_clamp;
     a.ctx_len = ctx_len;
     a.q = static_cast<const uint16_t *>(q);
     a.mul = mode == DUSTIN_SCORE_PROB_SUM ? (double)scale * 1.4426950408889634 : (double)scale;
     a.logits = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.logits_off);
     a.tile_max = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.max_off);
-    a.tile_sum = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.sum_off);
+    a.part_max = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.pmax_off);
+    a.part_sum = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.psum_off);
     a.score = score;
     int qh = 0, pr = 0;
     for (int i = 0; i < n_groups; ++i) {

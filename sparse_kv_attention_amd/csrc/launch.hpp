@@ -47,6 +47,8 @@ constexpr int kMaxGroups = 16;
 constexpr int kMaxPairsPerGroup = 64;       // logit-sum mode
 constexpr int kMaxProbPairsPerGroup = 16;   // softmax mode
 constexpr int kProbTile = 256;    // tokens per workgroup of the softmax-mode logit kernel
+constexpr int kStatTile = 64;     // tokens per statistics tile (one maximum per pair)
+constexpr int kScoreParts = 64;   // most workgroups per (group, sequence) of the softmax-mode logit kernel
 
 struct ScoreGroup {
     KvView k;
@@ -58,13 +60,14 @@ struct ScoreGroup {
 };
 
 struct ScoreArgs {
-    int B, n_max, n_pad, n_groups, n_q, mode, total_qheads, total_pairs, n_tiles, ctx_clamp;
+    int B, n_max, n_pad, n_groups, n_q, mode, total_qheads, total_pairs, n_tiles, n_parts, ctx_clamp;
     const int32_t *ctx_len;
     const uint16_t *q;
     double mul;              // PROB_SUM: scale*log2(e) (base-2 logits); LOGIT_SUM2: scale
     float *logits;           // [B][total_pairs][n_pad]: PROB_SUM l - tile max; LOGIT_SUM2 l
-    double *tile_max;        // PROB_SUM: [B][total_pairs][n_tiles]
-    float *tile_sum;         // PROB_SUM: [B][total_pairs][n_tiles], sum of exp2(l - tile max)
+    double *tile_max;        // PROB_SUM: [B][total_pairs][n_tiles], n_tiles = ceil(n_max / kStatTile)
+    double *part_max;        // PROB_SUM: [B][total_pairs][n_parts], one (max, sum of exp2(l - max))
+    double *part_sum;        //   per workgroup of the logit kernel
     float *score;            // [B][n_max]
     ScoreGroup grp[kMaxGroups];
 };

@@ -4,19 +4,24 @@
 // Vegas summary 2A/2B for the logit-sum mode over the first and bonus queries).
 //
 // Softmax mode (PROB_SUM), two kernels:
-//   srh_prob_logits  one workgroup per (256-token tile, group, sequence).  The tile's key
-//                    rows are read with coalesced 16-byte loads into LDS; each thread then
-//                    owns one token and forms its logits for the group's (query head,
-//                    query) pairs with fp64 FMAs (bf16 x bf16 products are exact in fp64,
-//                    so the only rounding left is fp64 accumulation).  Logits are stored
-//                    as fp32 offsets from the tile's per-pair maximum, so tokens near the
+//   srh_prob_logits  one workgroup per (run of 256-token tiles, group, sequence); the grid
+//                    is sized to one resident round.  A tile's key rows are read with
+//                    coalesced non-temporal 16-byte loads into LDS, the next tile is
+//                    prefetched into registers.  The four lanes of a quad share four
+//                    tokens and split the head dim, so each fp64 query value read from LDS
+//                    feeds several tokens; the quad's partial dot products are combined by
+//                    a DPP reduce-scatter, after which lane t holds token t of the tile.
+//                    Products of bf16 values are exact in fp64, so the only rounding is
+//                    fp64 accumulation.  Logits are stored as fp32 offsets from the maximum
+//                    of their 64-token statistics tile (one wave), so tokens near the
 //                    maximum — the ones that carry probability mass — keep full relative
-//                    precision even when logits are large; the tile leaves (max, sum of
-//                    exp2) per pair.
-//   srh_finalize     one workgroup per (1024 tokens, sequence): per pair (one wave per
-//                    pair, lanes over tiles) the global max and 1/Z from the tile
-//                    partials, then per token the sum over pairs of
-//                    exp2(offset + tile max - max) / Z.
+//                    precision even when logits are large.  Every tile leaves its maximum
+//                    per pair; every workgroup leaves one (max, sum of exp2) per pair over
+//                    all its tiles.
+//   srh_finalize     one workgroup per (1024 tokens, sequence): per pair, the global max
+//                    and 1/Z from the workgroup partials (one wave per pair, loads of
+//                    several pairs in flight together), then per token the sum over pairs
+//                    of exp2(offset + tile max - max) / Z.
 // Logit-sum mode (LOGIT_SUM2): srh_logit_sum computes the raw scaled logits on MFMA (bf16
 // in, fp32 accumulate; the sum's tolerance scales with the sum of |logits|), and the
 // finalize kernel sums them per token.
@@ -30,35 +35,84 @@ namespace dustin {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kProbTilesPerWg = 4;         // tiles each softmax-mode workgroup streams
 
-__device__ __forceinline__ double wave_max_f64(double v)
+// Whole-wave reductions without LDS: quad_perm xor 1 and xor 2, row_half_mirror (the other
+// quad of the 8 lanes), row_mirror (the other half of the 16-lane row), then the
+// permlane16 / permlane32 swaps across rows.  Every lane ends with the result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = fmax(v, __shfl_xor(v, o));
-    return v;
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
 }
 
-__device__ __forceinline__ float wave_sum_f32(float v)
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
-    return v;
+    const uint64_t u = __double_as_longlong(v);
+    const uint64_t lo = dpp32<CTRL>((uint32_t)u), hi = dpp32<CTRL>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+__device__ __forceinline__ double swap_max_f64(double v, bool wide)
+{
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    const auto a = wide ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                        : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = wide ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                        : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const double x = __longlong_as_double((long long)(((uint64_t)b[0] << 32) | a[0]));
+    const double y = __longlong_as_double((long long)(((uint64_t)b[1] << 32) | a[1]));
+    return fmax(x, y);
+}
+
+__device__ __forceinline__ double wave_max_f64_dpp(double v)
+{
+    v = fmax(v, dpp64<0xB1>(v));
+    v = fmax(v, dpp64<0x4E>(v));
+    v = fmax(v, dpp64<0x141>(v));
+    v = fmax(v, dpp64<0x140>(v));
+    v = swap_max_f64(v, false);
+    return swap_max_f64(v, true);
+}
+
+__device__ __forceinline__ float wave_sum_f32_dpp(float v)
+{
+    v += __uint_as_float(dpp32<0xB1>(__float_as_uint(v)));
+    v += __uint_as_float(dpp32<0x4E>(__float_as_uint(v)));
+    v += __uint_as_float(dpp32<0x141>(__float_as_uint(v)));
+    v += __uint_as_float(dpp32<0x140>(__float_as_uint(v)));
+    const uint32_t u = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const uint32_t u2 = __float_as_uint(v);
+    const auto c = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// v from the lane whose index differs in bit log2(X) (X = 1 or 2), within the quad
+template <int X>
+__device__ __forceinline__ double quad_xor(double v)
+{
+    constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+    const uint64_t u = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, ctrl, 0xF, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), ctrl, 0xF, 0xF, true);
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
 template <int D, int PC>
-__global__ __launch_bounds__(kThreads) void srh_prob_logits_kernel(ScoreArgs a)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8 ? 1 : 2))) void srh_prob_logits_kernel(ScoreArgs a)
 {
+    constexpr int KT = (PC > 8 || D > 64) ? 2 : 4;   // tokens converted to fp64 at once
     constexpr int RB = D * 2;          // bytes per key row
     constexpr int RSTR = RB + 16;      // LDS row stride (conflict-free 16-byte row reads)
     constexpr int CPR = RB / 16;       // 16-byte chunks per row
     constexpr int LPT = kProbTile * CPR / kThreads;   // 16-byte loads per thread per tile
     __shared__ __align__(16) uint8_t sK[kProbTile * RSTR];
     __shared__ __align__(16) double sQ[PC][D];
-    __shared__ double sMx[4][PC];
-    __shared__ float sSm[4][PC];
+    __shared__ double sRunM[4][PC];   // per wave: running max and sum of exp2(l - max)
+    __shared__ double sRunS[4][PC];
 
     const ScoreGroup &G = a.grp[blockIdx.y];
     const int b = blockIdx.z;
@@ -68,15 +122,22 @@ __global__ __launch_bounds__(kThreads) void srh_prob_logits_kernel(ScoreArgs a)
     const int lane = tid & 63;
     const int n_live = (N + kProbTile - 1) / kProbTile;     // tiles holding context tokens
 
-    // tiles past the context: empty partials
-    for (int tile = n_live + blockIdx.x; tile < a.n_tiles; tile += gridDim.x)
+    // statistics tiles past the live tiles: empty partials
+    for (int st = n_live * (kProbTile / kStatTile) + blockIdx.x; st < a.n_tiles; st += gridDim.x)
         for (int p = tid; p < G.n_pairs; p += kThreads) {
-            const int64_t st = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_tiles + tile;
-            a.tile_max[st] = -INFINITY;
-            a.tile_sum[st] = 0.f;
+            const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_tiles + st;
+            a.tile_max[e] = -INFINITY;
         }
-    if ((int)blockIdx.x >= n_live)
+    if ((int)blockIdx.x >= n_live) {
+        for (int p = tid; p < G.n_pairs; p += kThreads) {
+            const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_parts + blockIdx.x;
+            a.part_max[e] = -INFINITY;
+            a.part_sum[e] = 0.0;
+        }
         return;
+    }
+    // running (max, sum of exp2(l - max)) of the wave's tiles: lane p holds pair p
+    double runM = -INFINITY, runS = 0.0;
 
     // the group's queries (fp64) stay in LDS for every tile of this workgroup
     for (int e = tid; e < PC * D; e += kThreads) {
@@ -101,7 +162,8 @@ __global__ __launch_bounds__(kThreads) void srh_prob_logits_kernel(ScoreArgs a)
             const int c = tid + i * kThreads;
             const int r = c / CPR;
             const int t = t0 + r;
-            kr[i] = t < N ? load16(G.k.base + kv_offset(G.k, b, t, G.kv_head) + (c - r * CPR) * 8)
+            kr[i] = t < N ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                                G.k.base + kv_offset(G.k, b, t, G.kv_head) + (c - r * CPR) * 8))
                           : u32x4{0, 0, 0, 0};
         }
     };
@@ -119,57 +181,111 @@ __global__ __launch_bounds__(kThreads) void srh_prob_logits_kernel(ScoreArgs a)
             issue(tile + gridDim.x);      // next tile in flight during this tile's math
         __syncthreads();
 
-        const int tok = tile * kProbTile + tid;
-        const bool valid = tok < N;
-        const uint8_t *row = &sK[tid * RSTR];
-        double acc[PC];
+        // Dot products: the four lanes of a quad share tokens 4g .. 4g+3 and split the head
+        // dim, lane s taking the 16-byte chunks 4j+s (so one quad reads four different
+        // chunks of the query and the 16 lanes of an LDS pass hit distinct banks).  Each
+        // query value read from LDS feeds four tokens.
+        const int g = tid >> 2;
+        const int s = tid & 3;
+        double acc[4][PC];
 #pragma unroll
-        for (int p = 0; p < PC; ++p)
-            acc[p] = 0.0;
-#pragma unroll 2
-        for (int dd = 0; dd < D; dd += 8) {
-            const u32x4 kw = *reinterpret_cast<const u32x4 *>(row + dd * 2);
-            double kv[8];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kv[2 * j] = (double)bf16_lo(kw[j]);
-                kv[2 * j + 1] = (double)bf16_hi(kw[j]);
-            }
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int p = 0; p < PC; ++p)
+                acc[i][p] = 0.0;
+#pragma unroll 1
+        for (int j = 0; j < CPR / 4; ++j) {
+            const int ch = 4 * j + s;
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[p] = fma(kv[j], sQ[p][dd + j], acc[p]);
+            for (int i0 = 0; i0 < 4; i0 += KT) {
+                double kv[KT][8];
+#pragma unroll
+                for (int i = 0; i < KT; ++i) {
+                    const u32x4 kw = *reinterpret_cast<const u32x4 *>(&sK[(4 * g + i0 + i) * RSTR + ch * 16]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        kv[i][2 * e] = (double)bf16_lo(kw[e]);
+                        kv[i][2 * e + 1] = (double)bf16_hi(kw[e]);
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < PC; ++p) {
+                    double qv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        qv[e] = sQ[p][8 * ch + e];
+#pragma unroll
+                    for (int i = 0; i < KT; ++i)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            acc[i0 + i][p] = fma(kv[i][e], qv[e], acc[i0 + i][p]);
+                    __builtin_amdgcn_sched_barrier(0);   // keep one pair's query values live at a time
+                }
+            }
         }
-
-        // ---- per-pair tile maximum (fp64), offsets from it, sum of exp2 ----
+        // reduce-scatter over the quad: lane s ends with the full sums of token 4g+s
+        const int tok = tile * kProbTile + tid;
+        const bool valid = tok < N;
         double l[PC];
 #pragma unroll
         for (int p = 0; p < PC; ++p) {
-            l[p] = valid ? acc[p] * a.mul : -INFINITY;
-            const double m = wave_max_f64(l[p]);
-            if (lane == 0)
-                sMx[w][p] = m;
+            const bool hi2 = s & 2;
+            double keep[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const double mine = hi2 ? acc[2 + k][p] : acc[k][p];
+                const double give = hi2 ? acc[k][p] : acc[2 + k][p];
+                keep[k] = mine + quad_xor<2>(give);
+            }
+            const bool hi1 = s & 1;
+            const double mine = hi1 ? keep[1] : keep[0];
+            const double give = hi1 ? keep[0] : keep[1];
+            l[p] = mine + quad_xor<1>(give);
         }
-        __syncthreads();
+
+        // ---- per wave (its 64 tokens are one statistics tile): per-pair maximum (fp64),
+        // offsets from it, sum of exp2 ----
+        const int stile = tile * (kProbTile / kStatTile) + w;
 #pragma unroll
         for (int p = 0; p < PC; ++p) {
-            const double m = fmax(fmax(sMx[0][p], sMx[1][p]), fmax(sMx[2][p], sMx[3][p]));
-            const float off = valid ? (float)(l[p] - m) : -INFINITY;
-            const float s = wave_sum_f32(valid ? fast_exp2(off) : 0.f);
-            if (lane == 0)
-                sSm[w][p] = s;
-            if (valid && p < G.n_pairs)
-                a.logits[((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_pad + tok] = off;
+            const double lp = valid ? l[p] * a.mul : -INFINITY;
+            const double m = wave_max_f64_dpp(lp);
+            const float off = valid ? (float)(lp - m) : -INFINITY;
+            const float sm = wave_sum_f32_dpp(valid ? fast_exp2(off) : 0.f);
+            if (p < G.n_pairs) {
+                const int64_t row = (int64_t)b * a.total_pairs + G.pair0 + p;
+                if (valid)
+                    a.logits[row * a.n_pad + tok] = off;
+                if (lane == 0 && stile < a.n_tiles)   // a wave past n_tiles holds no token
+                    a.tile_max[row * a.n_tiles + stile] = m;
+            }
+            if (lane == p && m > -INFINITY) {   // fold the tile into the running pair
+                const double M1 = fmax(runM, m);
+                const double s0 = runM > -INFINITY ? runS * (double)fast_exp2((float)(runM - M1)) : 0.0;
+                runS = s0 + (double)sm * (double)fast_exp2((float)(m - M1));
+                runM = M1;
+            }
         }
-        __syncthreads();
-        if (tid < G.n_pairs && tid < PC) {
-            const int p = tid;
-            const double m = fmax(fmax(sMx[0][p], sMx[1][p]), fmax(sMx[2][p], sMx[3][p]));
-            const int64_t st = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_tiles + tile;
-            a.tile_max[st] = m;
-            a.tile_sum[st] = (sSm[0][p] + sSm[1][p]) + (sSm[2][p] + sSm[3][p]);
-        }
+    }
+    if (lane < PC) {
+        sRunM[w][lane] = runM;
+        sRunS[w][lane] = runS;
+    }
+    __syncthreads();
+    if (tid < G.n_pairs) {   // this workgroup's (max, sum) per pair, over its waves
+        const int p = tid;
+        double M = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            M = fmax(M, sRunM[v][p]);
+        double S = 0.0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            if (sRunM[v][p] > -INFINITY)
+                S += sRunS[v][p] * (double)fast_exp2((float)(sRunM[v][p] - M));
+        const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_parts + blockIdx.x;
+        a.part_max[e] = M;
+        a.part_sum[e] = S;
     }
 }
 
@@ -262,40 +378,50 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
 }
 
 constexpr int kFinTokens = 1024;
-constexpr int kFinTiles = kFinTokens / kProbTile;
+constexpr int kFinTiles = kFinTokens / kStatTile;
+constexpr int kFinBatch = 8;               // pairs per wave whose loads are in flight together
 
 __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
 {
-    __shared__ float sOff[kMaxGroups * kMaxPairsPerGroup][kFinTiles];
-    __shared__ float sInvZ[kMaxGroups * kMaxPairsPerGroup];
+    __shared__ float sOff[kMaxGroups * kMaxProbPairsPerGroup][kFinTiles];
+    __shared__ float sInvZ[kMaxGroups * kMaxProbPairsPerGroup];
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
     const int N = clampi(a.ctx_len[b], 0, a.ctx_clamp);
     const bool prob = a.mode == DUSTIN_SCORE_PROB_SUM;
     const int tile0 = blockIdx.x * kFinTiles;
     if (prob) {
-        // one wave per pair: lanes take the tiles; the max (fp64) and the normaliser (fp32
-        // exp2 of the fp64 difference, summed in fp64) are reduced across the wave
+        // one wave per pair, kFinBatch pairs at a time with all their loads issued together:
+        // lanes take the workgroup partials (at most kScoreParts) for the pair's max (fp64)
+        // and normaliser (fp32 exp2 of the fp64 difference, summed in fp64), and lanes below
+        // kFinTiles the maxima of this block's statistics tiles
         const int w = tid >> 6, lane = tid & 63;
-        for (int p = w; p < a.total_pairs; p += kThreads / 64) {
-            const double *mx = a.tile_max + ((int64_t)b * a.total_pairs + p) * a.n_tiles;
-            const float *sm = a.tile_sum + ((int64_t)b * a.total_pairs + p) * a.n_tiles;
-            double M = -INFINITY;
-            for (int t = lane; t < a.n_tiles; t += 64)
-                M = fmax(M, mx[t]);
-            M = wave_max_f64(M);
-            double Z = 0.0;
-            for (int t = lane; t < a.n_tiles; t += 64)
-                if (sm[t] > 0.f)
-                    Z += (double)sm[t] * (double)fast_exp2((float)(mx[t] - M));
+        const int t = tile0 + lane;
+        for (int p0 = w; p0 < a.total_pairs; p0 += 4 * kFinBatch) {
+            double pm[kFinBatch], ps[kFinBatch], tm[kFinBatch];
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1)
-                Z += __shfl_xor(Z, o);
-            if (lane == 0)
-                sInvZ[p] = Z > 0.0 ? (float)(1.0 / Z) : 0.f;
-            if (lane < kFinTiles) {
-                const int t = tile0 + lane;
-                sOff[p][lane] = t < a.n_tiles && mx[t] > -INFINITY ? (float)(mx[t] - M) : 0.f;
+            for (int k = 0; k < kFinBatch; ++k) {
+                const int p = p0 + 4 * k;
+                const int64_t row = (int64_t)b * a.total_pairs + p;
+                const bool ok = p < a.total_pairs;
+                pm[k] = ok && lane < a.n_parts ? a.part_max[row * a.n_parts + lane] : -INFINITY;
+                ps[k] = ok && lane < a.n_parts ? a.part_sum[row * a.n_parts + lane] : 0.0;
+                tm[k] = ok && lane < kFinTiles && t < a.n_tiles ? a.tile_max[row * a.n_tiles + t] : -INFINITY;
+            }
+#pragma unroll
+            for (int k = 0; k < kFinBatch; ++k) {
+                const int p = p0 + 4 * k;
+                const double M = wave_max_f64_dpp(pm[k]);
+                double Z = ps[k] > 0.0 ? ps[k] * (double)fast_exp2((float)(pm[k] - M)) : 0.0;
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1)
+                    Z += __shfl_xor(Z, o);
+                if (p < a.total_pairs) {
+                    if (lane == 0)
+                        sInvZ[p] = Z > 0.0 ? (float)(1.0 / Z) : 0.f;
+                    if (lane < kFinTiles)
+                        sOff[p][lane] = tm[k] > -INFINITY ? (float)(tm[k] - M) : 0.f;
+                }
             }
         }
         __syncthreads();
@@ -303,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
     const int tb = blockIdx.x * kFinTokens + tid * 4;
     if (tb >= a.n_max)
         return;
-    const int tl = (tid * 4) / kProbTile;   // tile of these 4 tokens within the block
+    const int tl = (tid * 4) / kStatTile;   // statistics tile of these 4 tokens within the block
     f32x4 v{0.f, 0.f, 0.f, 0.f};
     if (tb < N) {
         const float *lg = a.logits + (int64_t)b * a.total_pairs * a.n_pad + tb;
@@ -369,7 +495,7 @@ hipError_t launch_score(const ScoreArgs &a, int head_dim, int max_pairs, hipStre
 {
     hipError_t e = hipSuccess;
     if (a.mode == DUSTIN_SCORE_PROB_SUM) {
-        const dim3 g1((unsigned)((a.n_tiles + kProbTilesPerWg - 1) / kProbTilesPerWg), (unsigned)a.n_groups,
+        const dim3 g1((unsigned)a.n_parts, (unsigned)a.n_groups,
                       (unsigned)a.B);
         if (head_dim == 64)
             e = launch_prob<64>(a, max_pairs, g1, st);
