@@ -101,10 +101,18 @@ __device__ __forceinline__ double quad_xor(double v)
     return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
-template <int D, int PC>
+// FLAT: every group's view is unpaged with a row stride below 4 GiB, so a row address is a
+// per-workgroup base plus token x stride (one 32x32->64 multiply-add per load).
+template <int D, int PC, bool FLAT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8 ? 1 : 2))) void srh_prob_logits_kernel(ScoreArgs a)
 {
-    constexpr int KT = (PC > 8 || D > 64) ? 2 : 4;   // tokens converted to fp64 at once
+    // lanes per token group = tokens per lane: 4 where registers allow (each query value
+    // then feeds four tokens), 2 for the 128-wide rows (two tiles of them are in flight)
+    constexpr int S = (D > 64 || PC > 8) ? 2 : 4;
+    constexpr int KT = S;                  // tokens converted to fp64 at once
+    // tiles in flight in registers: two where the registers hold them (row addresses are
+    // then one multiply-add each), else one
+    constexpr int kDepth = (FLAT && (D == 64 || PC <= 5)) ? 2 : 1;
     constexpr int RB = D * 2;          // bytes per key row
     constexpr int RSTR = RB + 16;      // LDS row stride (conflict-free 16-byte row reads)
     constexpr int CPR = RB / 16;       // 16-byte chunks per row
@@ -154,22 +162,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
     }
 
     // tile rows: thread tid loads chunks tid + i*256 (row = chunk / CPR), all issued at once
-    u32x4 kr[LPT];
-    auto issue = [&](int tile) {
+    // kDepth tiles in flight in registers per thread.  Loads are unconditional (positions
+    // past the context read row N-1, which is discarded), so the waits count exactly.
+    const char *flat_base = reinterpret_cast<const char *>(G.k.base + (int64_t)b * G.k.sb + (int64_t)G.kv_head * G.k.sh) +
+                            (tid % CPR) * 16;
+    const uint32_t flat_st = (uint32_t)(G.k.st * 2);
+    auto issue = [&](u32x4 (&kr)[LPT], int tile) {
         const int t0 = tile * kProbTile;
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
             const int c = tid + i * kThreads;
             const int r = c / CPR;
-            const int t = t0 + r;
-            kr[i] = t < N ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                                G.k.base + kv_offset(G.k, b, t, G.kv_head) + (c - r * CPR) * 8))
-                          : u32x4{0, 0, 0, 0};
+            const int t = min(t0 + r, N - 1);
+            const u32x4 *src;
+            if constexpr (FLAT)
+                src = reinterpret_cast<const u32x4 *>(flat_base + (uint64_t)(uint32_t)t * flat_st);
+            else
+                src = reinterpret_cast<const u32x4 *>(G.k.base + kv_offset(G.k, b, t, G.kv_head) + (c - r * CPR) * 8);
+            kr[i] = __builtin_nontemporal_load(src);
         }
     };
-    int tile = blockIdx.x;
-    issue(tile);
-    for (; tile < n_live; tile += gridDim.x) {
+    auto stage = [&](const u32x4 (&kr)[LPT]) {
         __syncthreads();                  // previous tile's rows consumed
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
@@ -177,31 +190,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
             const int r = c / CPR;
             *reinterpret_cast<u32x4 *>(&sK[r * RSTR + (c - r * CPR) * 16]) = kr[i];
         }
-        if (tile + (int)gridDim.x < n_live)
-            issue(tile + gridDim.x);      // next tile in flight during this tile's math
+    };
+    auto process = [&](int tile) {
         __syncthreads();
 
-        // Dot products: the four lanes of a quad share tokens 4g .. 4g+3 and split the head
-        // dim, lane s taking the 16-byte chunks 4j+s (so one quad reads four different
-        // chunks of the query and the 16 lanes of an LDS pass hit distinct banks).  Each
-        // query value read from LDS feeds four tokens.
-        const int g = tid >> 2;
-        const int s = tid & 3;
-        double acc[4][PC];
+        // Dot products: S lanes share the S tokens S*g .. S*g+S-1 and split the head dim,
+        // lane s taking the 16-byte chunks S*j+s (so the 16 lanes of an LDS pass hit
+        // distinct banks).  Each query value read from LDS feeds KT tokens.
+        const int g = tid / S;
+        const int s = tid % S;
+        double acc[S][PC];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < S; ++i)
 #pragma unroll
             for (int p = 0; p < PC; ++p)
                 acc[i][p] = 0.0;
 #pragma unroll 1
-        for (int j = 0; j < CPR / 4; ++j) {
-            const int ch = 4 * j + s;
+        for (int j = 0; j < CPR / S; ++j) {
+            const int ch = S * j + s;
 #pragma unroll
-            for (int i0 = 0; i0 < 4; i0 += KT) {
+            for (int i0 = 0; i0 < S; i0 += KT) {
                 double kv[KT][8];
 #pragma unroll
                 for (int i = 0; i < KT; ++i) {
-                    const u32x4 kw = *reinterpret_cast<const u32x4 *>(&sK[(4 * g + i0 + i) * RSTR + ch * 16]);
+                    const u32x4 kw = *reinterpret_cast<const u32x4 *>(&sK[(S * g + i0 + i) * RSTR + ch * 16]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         kv[i][2 * e] = (double)bf16_lo(kw[e]);
@@ -223,19 +235,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
                 }
             }
         }
-        // reduce-scatter over the quad: lane s ends with the full sums of token 4g+s
+        // reduce-scatter over the S lanes: lane s ends with the full sums of token S*g+s,
+        // i.e. lane tid holds token tid of the tile
         const int tok = tile * kProbTile + tid;
         const bool valid = tok < N;
         double l[PC];
 #pragma unroll
         for (int p = 0; p < PC; ++p) {
-            const bool hi2 = s & 2;
             double keep[2];
+            if constexpr (S == 4) {
+                const bool hi2 = s & 2;
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const double mine = hi2 ? acc[2 + k][p] : acc[k][p];
-                const double give = hi2 ? acc[k][p] : acc[2 + k][p];
-                keep[k] = mine + quad_xor<2>(give);
+                for (int k = 0; k < 2; ++k) {
+                    const double mine = hi2 ? acc[2 + k][p] : acc[k][p];
+                    const double give = hi2 ? acc[k][p] : acc[2 + k][p];
+                    keep[k] = mine + quad_xor<2>(give);
+                }
+            } else {
+                keep[0] = acc[0][p];
+                keep[1] = acc[1][p];
             }
             const bool hi1 = s & 1;
             const double mine = hi1 ? keep[1] : keep[0];
@@ -265,6 +283,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
                 runS = s0 + (double)sm * (double)fast_exp2((float)(m - M1));
                 runM = M1;
             }
+        }
+    };
+    const int step = gridDim.x;
+    int tile = blockIdx.x;
+    u32x4 krA[LPT];
+    issue(krA, tile);
+    if constexpr (kDepth == 2) {
+        u32x4 krB[LPT];
+        __builtin_amdgcn_sched_barrier(0);   // krA's loads first, as in the loop
+        issue(krB, tile + step);
+        // one exit: the second half of the last pair may lie past the live tiles (its
+        // staged rows are then discarded)
+        const int pairs_of_tiles = ((n_live - tile + step - 1) / step + 1) / 2;
+        for (int k = 0; k < pairs_of_tiles; ++k) {
+            stage(krA);
+            issue(krA, tile + 2 * step);
+            process(tile);
+            stage(krB);
+            issue(krB, tile + 3 * step);
+            if (tile + step < n_live)
+                process(tile + step);
+            tile += 2 * step;
+        }
+    } else {
+        for (;;) {
+            stage(krA);
+            issue(krA, tile + step);
+            process(tile);
+            tile += step;
+            if (tile >= n_live)
+                break;
         }
     }
     if (lane < PC) {
@@ -476,16 +525,27 @@ hipError_t launch_logit_sum(const ScoreArgs &a, int pt, dim3 grid, hipStream_t s
 template <int D>
 hipError_t launch_prob(const ScoreArgs &a, int max_pairs, dim3 grid, hipStream_t st)
 {
+    bool flat = true;
+    for (int g = 0; g < a.n_groups; ++g)
+        flat = flat && !a.grp[g].k.pt && a.grp[g].k.st >= 0 && a.grp[g].k.st * 2 < (int64_t)1 << 32;
+#define DUSTIN_PROB(PCV)                                                                            \
+    do {                                                                                            \
+        if (flat)                                                                                   \
+            hipLaunchKernelGGL((srh_prob_logits_kernel<D, PCV, true>), grid, dim3(kThreads), 0, st, a);  \
+        else                                                                                        \
+            hipLaunchKernelGGL((srh_prob_logits_kernel<D, PCV, false>), grid, dim3(kThreads), 0, st, a); \
+    } while (0)
     if (max_pairs <= 4)
-        hipLaunchKernelGGL((srh_prob_logits_kernel<D, 4>), grid, dim3(kThreads), 0, st, a);
+        DUSTIN_PROB(4);
     else if (max_pairs <= 5)
-        hipLaunchKernelGGL((srh_prob_logits_kernel<D, 5>), grid, dim3(kThreads), 0, st, a);
+        DUSTIN_PROB(5);
     else if (max_pairs <= 8)
-        hipLaunchKernelGGL((srh_prob_logits_kernel<D, 8>), grid, dim3(kThreads), 0, st, a);
+        DUSTIN_PROB(8);
     else if (max_pairs <= 16)
-        hipLaunchKernelGGL((srh_prob_logits_kernel<D, 16>), grid, dim3(kThreads), 0, st, a);
+        DUSTIN_PROB(16);
     else
         return hipErrorInvalidValue;
+#undef DUSTIN_PROB
     return hipGetLastError();
 }
 
