@@ -34,6 +34,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 32;          // list positions per wave step
+constexpr int kNewWave = 3;        // wave of the last split that takes the new-token step (it
+                                   // has the fewest ring steps)
 constexpr float kLazy = 8.f;       // rescale O only when a tile's max exceeds the reference by 2^8
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -93,10 +95,11 @@ struct AttnShape {
     using G = Geo<D>;
     static constexpr int QR = QT * 16;          // padded query rows
     static constexpr int ACC = G::DVT * QT * 4; // O accumulator floats per lane
-    static constexpr int TAB = kSplitMax * 8;
+    static constexpr int TAB = (kSplitMax + 32) * 8;   // + the new-token rows' K and V offsets
     static constexpr int RING = 4 * R * G::SLOT;
     static constexpr int MRG = 4 * 64 * ACC * 4 + 2 * 4 * QR * 4;
-    static constexpr int LDS = TAB + (RING > MRG ? RING : MRG);
+    static constexpr int NEW = TAB + (RING > MRG ? RING : MRG);   // new-token rows: 16 K, 16 V
+    static constexpr int LDS = NEW + 2 * 16 * G::RB;
     static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
     for (int k = 0; k < PT; ++k) {
         const int i = tid + k * kThreads;
         const int pos = p0 + i;
-        raw[k] = (a.idx && i < a.spl + a.nv && pos < a.k_max) ? a.idx[(int64_t)b * a.k_max + pos] : 0;
+        raw[k] = (a.idx && i < a.spl && pos < a.k_max) ? a.idx[(int64_t)b * a.k_max + pos] : 0;
     }
     const int n_raw = a.ctx_len[b];
     const int c_raw = a.idx ? a.count[b] : 0;
@@ -176,13 +179,14 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
     // ---- sequence geometry; every device value is clamped ----
     const int N = clampi(n_raw, 0, a.ctx_clamp);
     const int nsel = a.idx ? clampi(c_raw, 0, min(a.k_max, N)) : N;
-    const int L = nsel + a.nv;
-    // split ranges are sized on the selected positions; the last split also takes the
-    // new-token block (at most nv positions beyond its size)
-    const int p1 = split == a.splits - 1 ? L : min(p0 + a.spl, L);
+    // split ranges cover the selected positions; the new-token block (nv <= 16 rows,
+    // list positions nsel .. nsel+nv-1) is a separate 16-row step of one wave of the last
+    // split, loaded at the start into its own LDS area so that no wave's ring carries an
+    // extra step
+    const int p1 = min(p0 + a.spl, nsel);
     const int cnt = max(p1 - p0, 0);
-    const int full_end = min(p1, nsel);   // positions below this need no mask
     const int ntile = (cnt + kTile - 1) / kTile;
+    const bool new_here = split == a.splits - 1 && w == kNewWave;
 
     // ---- row offsets of the split's positions; the padding of the last step points at
     //      token N (the first new token, always present), whose scores are masked.  Paged
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
         const int pos = p0 + i;
         int tok = N;
         if (i < cnt)
-            tok = pos < nsel ? (a.idx ? clampi(raw[k], 0, N - 1) : pos) : N + (pos - nsel);
+            tok = a.idx ? clampi(raw[k], 0, N - 1) : pos;
         tokv[k] = tok;
     }
     int pgK[PT], pgV[PT];
@@ -222,6 +226,15 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
                                   : (int64_t)b * a.v.sb + (int64_t)tok * a.v.st;
         }
     }
+    // the new-token rows' offsets (last split): entry e of 16 is LDS row (e % n') * RPI +
+    // e / n' of the new-token area (n' = NI/2 DMA instructions), i.e. new token min(row,
+    // nv-1); K entries first, then V
+    if (split == a.splits - 1 && tid < 32) {
+        constexpr int NH = G::NI / 2;
+        const int e = tid & 15;
+        const int tok = N + min((e % NH) * G::RPI + e / NH, a.nv - 1);
+        sOffK[kSplitMax + tid] = tid < 16 ? kv_offset(a.k, b, tok, 0) : kv_offset(a.v, b, tok, 0);
+    }
     __syncthreads();                  // offset tables ready
 
     f32x4 acc[G::DVT][QT];
@@ -244,25 +257,33 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
     const int dg = lane / G::CPR;     // DMA: row group of the lane within an instruction
     const int dc = lane % G::CPR;     // DMA: LDS chunk of the lane within its row
 
-    // Step jj of this wave into ring slot jj % R: the lane moves rows dg*NI + n (n < NI)
-    // of the step, i.e. NI consecutive table entries.  Loads are non-temporal: every row
-    // is read once.
+    // ni instructions each of K and V rows into dst (V at dst + voff): the lane moves table
+    // entries tk[dg*ni + n] / tv[dg*ni + n] (n < ni) to LDS rows n*RPI + dg.  Loads are
+    // non-temporal: every row is read once.
+    auto dma_to = [&](const int64_t *tk, const int64_t *tv, uint8_t *dst, int voff, int ni) {
+#pragma unroll
+        for (int n = 0; n < G::NI; ++n) {
+            if (n < ni) {
+                const int rho = n * G::RPI + dg;
+                const int ck = dc ^ (rho % G::CPR);
+                __builtin_amdgcn_global_load_lds(kbase + tk[dg * ni + n] + ck * 8, (lds_void *)(dst + n * 1024), 16, 0,
+                                                 kLoadNonTemporal);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < G::NI; ++n) {
+            if (n < ni) {
+                const int rho = n * G::RPI + dg;
+                const int cv = dc ^ ((2 * rho) % G::CPR);
+                __builtin_amdgcn_global_load_lds(vbase + tv[dg * ni + n] + cv * 8, (lds_void *)(dst + voff + n * 1024),
+                                                 16, 0, kLoadNonTemporal);
+            }
+        }
+    };
+    // Step jj of this wave into ring slot jj % R (table entries of the step's 32 positions).
     auto dma = [&](int jj) {
-        const int e0 = (w + 4 * jj) * kTile + dg * G::NI;
-        uint8_t *slot = wring + (jj % R) * G::SLOT;
-#pragma unroll
-        for (int n = 0; n < G::NI; ++n) {
-            const int rho = n * G::RPI + dg;
-            const int ck = dc ^ (rho % G::CPR);
-            __builtin_amdgcn_global_load_lds(kbase + sOffK[e0 + n] + ck * 8, (lds_void *)(slot + n * 1024), 16, 0, kLoadNonTemporal);
-        }
-#pragma unroll
-        for (int n = 0; n < G::NI; ++n) {
-            const int rho = n * G::RPI + dg;
-            const int cv = dc ^ ((2 * rho) % G::CPR);
-            __builtin_amdgcn_global_load_lds(vbase + sOffV[e0 + n] + cv * 8,
-                                             (lds_void *)(slot + G::HALF + n * 1024), 16, 0, kLoadNonTemporal);
-        }
+        const int e0 = (w + 4 * jj) * kTile;
+        dma_to(sOffK + e0, sOffV + e0, wring + (jj % R) * G::SLOT, G::HALF, G::NI);
     };
 
     // per-lane LDS byte offsets of the operand reads (slot-relative)
@@ -291,11 +312,81 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
         for (int r = 0; r < 4; ++r)
             trow[h][r] = G::tau(16 * h + 4 * quad + r);
 
-    if (mine > 0) {
-        // All R slots are in flight while a step computes: a slot is refilled as soon as
-        // its K and V operands have been read into registers, before the step's math.
+    // The softmax and O^T update of one step, given its K and V^T operands.  S^T entry
+    // (h, r) is LDS row 16h + 4*quad + r of the step; its list position is pos0 +
+    // tau(row) for ring steps and pos0 + row for the new-token step (direct).  Entries at
+    // list positions >= pend, and new tokens after the query row's own, are masked.
+    auto math = [&](const u32x4 (&kop)[2][G::KS], const u32x4 (&vop)[G::DVT], bool full, int pos0,
+                    bool direct, int pend) {
+        // S^T = K Q^T for both 16-row halves of the step
+        f32x4 s[2][QT];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) {
+                s[h][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < G::KS; ++ks)
+                    s[h][qt] = mfma_bf16(kop[h][ks], qop[qt][ks], s[h][qt]);
+            }
+
+        u32x4 pb[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            if (!full) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int pos = pos0 + (direct ? 16 * h + 4 * quad + r : trow[h][r]);
+                        const bool ok = (pos < pend) & ((pos < nsel) | (pos - nsel <= qrow_t[qt]));
+                        s[h][qt][r] = ok ? s[h][qt][r] : -INFINITY;
+                    }
+            }
+            float mx = fmaxf(fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3])),
+                             fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
+            mx = max_over_quads(mx) * c;
+            if (__any(mx > mref[qt] + kLazy)) {
+                const float mnew = fmaxf(mref[qt], mx);
+                const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref[qt] - mnew);
+                mref[qt] = mnew;
+                lrun[qt] *= alpha;
+#pragma unroll
+                for (int i = 0; i < G::DVT; ++i)
+                    acc[i][qt] *= alpha;
+            }
+            const float nm = mref[qt] == -INFINITY ? 0.f : -mref[qt];
+            float p[2][4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p[h][r] = fast_exp2(fmaf(s[h][qt][r], c, nm));
+            lrun[qt] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+            pb[qt] = u32x4{cvt_pk_bf16(p[0][0], p[0][1]), cvt_pk_bf16(p[0][2], p[0][3]),
+                           cvt_pk_bf16(p[1][0], p[1][1]), cvt_pk_bf16(p[1][2], p[1][3])};
+        }
+        // O^T += V^T P^T over the 32 positions (16x16x32: k-slot (quad, 4h + r) is LDS
+        // row 16h + 4*quad + r in both operands)
+#pragma unroll
+        for (int dt = 0; dt < G::DVT; ++dt)
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt)
+                acc[dt][qt] = mfma_bf16(vop[dt], pb[qt], acc[dt][qt]);
+    };
+
+    // The new-token rows, requested first: LDS row rho (< 16) holds new token min(rho,
+    // nv-1) in the swizzled layout of a step's first half; the V rows follow the K rows.
+    uint8_t *nslot = lds + S::NEW;
+    if (new_here)
+        dma_to(sOffK + kSplitMax, sOffK + kSplitMax + 16, nslot, 16 * G::RB, G::NI / 2);
+
+    // All R slots are in flight while a step computes: a slot is refilled as soon as its K
+    // and V operands have been read into registers, before the step's math.
+    if (mine > 0)
         dma(0);
-        load_q();
+    load_q();
+    if (mine > 0) {
 #pragma unroll
         for (int jj = 1; jj < R; ++jj)
             if (jj < mine)
@@ -328,64 +419,26 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
                 __builtin_amdgcn_sched_barrier(0);
                 dma(jj + R);
             }
-
-            // S^T = K Q^T for both 16-row halves of the step
-            f32x4 s[2][QT];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int qt = 0; qt < QT; ++qt) {
-                    s[h][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < G::KS; ++ks)
-                        s[h][qt] = mfma_bf16(kop[h][ks], qop[qt][ks], s[h][qt]);
-                }
-
-            const bool full = pos0 + kTile <= full_end;
-            u32x4 pb[QT];
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) {
-                if (!full) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int pos = pos0 + trow[h][r];
-                            const bool ok = (pos < p1) & ((pos < nsel) | (pos - nsel <= qrow_t[qt]));
-                            s[h][qt][r] = ok ? s[h][qt][r] : -INFINITY;
-                        }
-                }
-                float mx = fmaxf(fmaxf(fmaxf(s[0][qt][0], s[0][qt][1]), fmaxf(s[0][qt][2], s[0][qt][3])),
-                                 fmaxf(fmaxf(s[1][qt][0], s[1][qt][1]), fmaxf(s[1][qt][2], s[1][qt][3])));
-                mx = max_over_quads(mx) * c;
-                if (__any(mx > mref[qt] + kLazy)) {
-                    const float mnew = fmaxf(mref[qt], mx);
-                    const float alpha = mnew == -INFINITY ? 1.f : fast_exp2(mref[qt] - mnew);
-                    mref[qt] = mnew;
-                    lrun[qt] *= alpha;
-#pragma unroll
-                    for (int i = 0; i < G::DVT; ++i)
-                        acc[i][qt] *= alpha;
-                }
-                const float nm = mref[qt] == -INFINITY ? 0.f : -mref[qt];
-                float p[2][4];
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        p[h][r] = fast_exp2(fmaf(s[h][qt][r], c, nm));
-                lrun[qt] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-                pb[qt] = u32x4{cvt_pk_bf16(p[0][0], p[0][1]), cvt_pk_bf16(p[0][2], p[0][3]),
-                               cvt_pk_bf16(p[1][0], p[1][1]), cvt_pk_bf16(p[1][2], p[1][3])};
-            }
-            // O^T += V^T P^T over the 32 positions (16x16x32: k-slot (quad, 4h + r) is LDS
-            // row 16h + 4*quad + r in both operands)
-#pragma unroll
-            for (int dt = 0; dt < G::DVT; ++dt)
-#pragma unroll
-                for (int qt = 0; qt < QT; ++qt)
-                    acc[dt][qt] = mfma_bf16(vop[dt], pb[qt], acc[dt][qt]);
+            math(kop, vop, pos0 + kTile <= p1, pos0, false, p1);
         }
+    }
+    if (new_here) {
+        // the new-token step: rows 16..31 have zero operands and are masked
+        wait_vmcnt<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 kop[2][G::KS];
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+            kop[0][ks] = *reinterpret_cast<const u32x4 *>(nslot + koff[0][ks]);
+            kop[1][ks] = u32x4{0, 0, 0, 0};
+        }
+        u32x4 vop[G::DVT];
+#pragma unroll
+        for (int dt = 0; dt < G::DVT; ++dt) {
+            const u32x2 v0 = lds_read_tr16(nslot + vrow[0] - G::HALF + 16 * G::RB + ((dt ^ vf2[0]) << 5));
+            vop[dt] = u32x4{v0[0], v0[1], 0, 0};
+        }
+        math(kop, vop, false, nsel, true, nsel + a.nv);
     }
 
     // ---- merge the four waves in one LDS exchange: every wave publishes its maxima,
@@ -578,11 +631,11 @@ AttnPlan plan_attn(int B, int Hkv, int G, int nv, int max_list, int target_wgs, 
     const int gv = G * nv;
     const int qt_total = (gv + 15) / 16;
     const int base = B * Hkv;
-    // Splits are sized on the selected positions (the whole context when dense); the last
-    // split also takes the new-token block, so a split holds at most split_cap - 32.
+    // Splits are sized on the selected positions (the whole context when dense); the
+    // new-token block is a separate step, so a split holds at most split_cap positions.
     const int sel = max(1, max_list - nv);
     const int target = max(1, target_wgs);
-    const int min_s = (sel + split_cap - 32 - 1) / (split_cap - 32);
+    const int min_s = (sel + split_cap - 1) / split_cap;
     // Query-row groups only as needed for the register budget: every group streams the
     // pair's K/V rows again.
     const int qg = (qt_total + kMaxQT - 1) / kMaxQT;

@@ -11,8 +11,8 @@ namespace dustin {
 
 // ---------------------------------------------------------------- attention
 constexpr int kMaxQT = 4;          // 16-row query tiles held by one workgroup
-constexpr int kSplitMax = 2080;    // list positions of one workgroup (65 steps of 32) when K and
-                                   // V rows share their offsets; half as many when they do not
+constexpr int kSplitMax = 2048;    // selected positions of one workgroup (64 steps of 32) when K
+                                   // and V rows share their offsets; half as many when they do not
 constexpr int kMaxSplits = 256;    // splits of one (sequence, KV head, query group)
 constexpr int kMaxList = 131072;   // longest list (selected positions + new tokens) accepted
 
