@@ -66,6 +66,38 @@ __device__ __forceinline__ double swap_max_f64(double v, bool wide)
     return fmax(x, y);
 }
 
+// In-place whole-wave max (MAX) or sum of N values per lane, all values through each step
+// together; every lane ends with the results.
+template <int N, bool MAX>
+__device__ __forceinline__ void wave_reduce_f32(float (&v)[N])
+{
+    auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = op(v[i], __uint_as_float(dpp32<0xB1>(__float_as_uint(v[i]))));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = op(v[i], __uint_as_float(dpp32<0x4E>(__float_as_uint(v[i]))));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = op(v[i], __uint_as_float(dpp32<0x141>(__float_as_uint(v[i]))));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = op(v[i], __uint_as_float(dpp32<0x140>(__float_as_uint(v[i]))));
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t u = __float_as_uint(v[i]);
+        const auto t = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        v[i] = op(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t u = __float_as_uint(v[i]);
+        const auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        v[i] = op(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    }
+}
+
 __device__ __forceinline__ double wave_max_f64_dpp(double v)
 {
     v = fmax(v, dpp64<0xB1>(v));
@@ -74,20 +106,6 @@ __device__ __forceinline__ double wave_max_f64_dpp(double v)
     v = fmax(v, dpp64<0x140>(v));
     v = swap_max_f64(v, false);
     return swap_max_f64(v, true);
-}
-
-__device__ __forceinline__ float wave_sum_f32_dpp(float v)
-{
-    v += __uint_as_float(dpp32<0xB1>(__float_as_uint(v)));
-    v += __uint_as_float(dpp32<0x4E>(__float_as_uint(v)));
-    v += __uint_as_float(dpp32<0x141>(__float_as_uint(v)));
-    v += __uint_as_float(dpp32<0x140>(__float_as_uint(v)));
-    const uint32_t u = __float_as_uint(v);
-    const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const uint32_t u2 = __float_as_uint(v);
-    const auto c = __builtin_amdgcn_permlane32_swap(u2, u2, false, false);
-    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
 // v from the lane whose index differs in bit log2(X) (X = 1 or 2), within the quad
@@ -261,28 +279,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
             l[p] = mine + quad_xor<1>(give);
         }
 
-        // ---- per wave (its 64 tokens are one statistics tile): per-pair maximum (fp64),
-        // offsets from it, sum of exp2 ----
+        // ---- per wave (its 64 tokens are one statistics tile): per-pair maximum, offsets
+        // from it, sum of exp2.  The maximum is taken over the fp32-rounded logits (rounding
+        // is monotonic, so it is the rounded true maximum); it is the tile's reference and
+        // the offsets are formed against it in fp64.  All pairs go through each reduction
+        // step together. ----
         const int stile = tile * (kProbTile / kStatTile) + w;
+        double lp[PC];
+        float mf[PC], off[PC], ex[PC];
 #pragma unroll
         for (int p = 0; p < PC; ++p) {
-            const double lp = valid ? l[p] * a.mul : -INFINITY;
-            const double m = wave_max_f64_dpp(lp);
-            const float off = valid ? (float)(lp - m) : -INFINITY;
-            const float sm = wave_sum_f32_dpp(valid ? fast_exp2(off) : 0.f);
-            if (p < G.n_pairs) {
-                const int64_t row = (int64_t)b * a.total_pairs + G.pair0 + p;
-                if (valid)
-                    a.logits[row * a.n_pad + tok] = off;
-                if (lane == 0 && stile < a.n_tiles)   // a wave past n_tiles holds no token
-                    a.tile_max[row * a.n_tiles + stile] = m;
-            }
-            if (lane == p && m > -INFINITY) {   // fold the tile into the running pair
-                const double M1 = fmax(runM, m);
-                const double s0 = runM > -INFINITY ? runS * (double)fast_exp2((float)(runM - M1)) : 0.0;
-                runS = s0 + (double)sm * (double)fast_exp2((float)(m - M1));
-                runM = M1;
-            }
+            lp[p] = valid ? l[p] * a.mul : -INFINITY;
+            mf[p] = (float)lp[p];
+        }
+        wave_reduce_f32<PC, true>(mf);
+#pragma unroll
+        for (int p = 0; p < PC; ++p) {
+            off[p] = valid ? (float)(lp[p] - (double)mf[p]) : -INFINITY;
+            ex[p] = valid ? fast_exp2(off[p]) : 0.f;
+        }
+        wave_reduce_f32<PC, false>(ex);
+        const int64_t row0 = (int64_t)b * a.total_pairs + G.pair0;
+#pragma unroll
+        for (int p = 0; p < PC; ++p)
+            if (p < G.n_pairs && valid)
+                a.logits[(row0 + p) * a.n_pad + tok] = off[p];
+        // lane p < PC takes pair p: it stores the tile maximum and folds the tile into its
+        // running (max, sum)
+        float m_l = mf[0], s_l = ex[0];
+#pragma unroll
+        for (int p = 1; p < PC; ++p) {
+            m_l = lane == p ? mf[p] : m_l;
+            s_l = lane == p ? ex[p] : s_l;
+        }
+        if (lane < G.n_pairs && lane < PC && stile < a.n_tiles)   // a wave past n_tiles holds no token
+            a.tile_max[(row0 + lane) * a.n_tiles + stile] = (double)m_l;
+        if (m_l > -INFINITY) {
+            const double m = (double)m_l;
+            const double M1 = fmax(runM, m);
+            const double s0 = runM > -INFINITY ? runS * (double)fast_exp2((float)(runM - M1)) : 0.0;
+            runS = s0 + (double)s_l * (double)fast_exp2((float)(m - M1));
+            runM = M1;
         }
     };
     const int step = gridDim.x;
