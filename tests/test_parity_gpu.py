@@ -112,6 +112,14 @@ def test_single_verify_query():
     check_pipeline(W.make_inputs(w, device="cuda"), [0], [0], [0, 1, 2])
 
 
+def test_widest_verify_block():
+    # 16 verify queries (the most accepted): the whole 16-row new-token step, causal inside
+    # it; G = 4 gives 64 query rows (four 16-row tiles) at head dim 128, and the head-dim-64
+    # draft streams score 15 lookahead queries
+    w = small("nv16", 2, 600, 8, 2, 128, 15, 128, 4, 16, 40, seed=16)
+    check_pipeline(W.make_inputs(w, device="cuda"), [0], [0], [0, 1])
+
+
 def test_query_groups_split():
     # G = 16 query heads per KV head x 8 verify queries = 128 rows: two query groups
     w = small("qgroups", 2, 400, 32, 2, 128, 7, 100, 4, 8, 20, seed=14)
