@@ -465,7 +465,8 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
 
 constexpr int kFinTokens = 1024;
 constexpr int kFinTiles = kFinTokens / kStatTile;
-constexpr int kFinBatch = 8;               // pairs per wave whose loads are in flight together
+constexpr int kFinBatch = 8;
+constexpr int kFinChunk = 32;              // pairs whose logits one finalize thread holds at once               // pairs per wave whose loads are in flight together
 
 __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
 {
@@ -476,6 +477,21 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
     const int N = clampi(a.ctx_len[b], 0, a.ctx_clamp);
     const bool prob = a.mode == DUSTIN_SCORE_PROB_SUM;
     const int tile0 = blockIdx.x * kFinTiles;
+    // this thread's 4 tokens: the logits of the first kFinChunk pairs are requested before
+    // the statistics (which do not need them), all in one round of loads
+    const int P = a.total_pairs;
+    const int tb = blockIdx.x * kFinTokens + tid * 4;
+    const bool live = tb < N;
+    const float *lg = a.logits + (int64_t)b * P * a.n_pad + tb;
+    f32x4 lv[kFinChunk];
+    auto fetch = [&](int p0) {
+#pragma unroll
+        for (int j = 0; j < kFinChunk; ++j) {
+            const int p = min(p0 + j, P - 1);
+            lv[j] = live ? *reinterpret_cast<const f32x4 *>(lg + (int64_t)p * a.n_pad) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    fetch(0);
     if (prob) {
         // one wave per pair, kFinBatch pairs at a time with all their loads issued together:
         // lanes take the workgroup partials (at most kScoreParts) for the pair's max (fp64)
@@ -512,29 +528,32 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
         }
         __syncthreads();
     }
-    const int tb = blockIdx.x * kFinTokens + tid * 4;
     if (tb >= a.n_max)
         return;
     const int tl = (tid * 4) / kStatTile;   // statistics tile of these 4 tokens within the block
     f32x4 v{0.f, 0.f, 0.f, 0.f};
-    if (tb < N) {
-        const float *lg = a.logits + (int64_t)b * a.total_pairs * a.n_pad + tb;
-        for (int p = 0; p < a.total_pairs; ++p) {
-            const f32x4 l = *reinterpret_cast<const f32x4 *>(lg + (int64_t)p * a.n_pad);
-            if (prob) {
-                const float c = sOff[p][tl], iz = sInvZ[p];
+    for (int p0 = 0; p0 < P; p0 += kFinChunk) {
+        if (p0 > 0)
+            fetch(p0);
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    v[r] += fast_exp2(l[r] + c) * iz;
-            } else {
-                v += l;
+        for (int j = 0; j < kFinChunk; ++j) {
+            const int p = p0 + j;
+            if (p < P) {
+                if (prob) {
+                    const float c = sOff[p][tl], iz = sInvZ[p];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] += fast_exp2(lv[j][r] + c) * iz;
+                } else {
+                    v += lv[j];
+                }
             }
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (tb + r >= N)
-                v[r] = 0.f;
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (tb + r >= N)
+            v[r] = 0.f;
     float *dst = a.score + (int64_t)b * a.n_max + tb;
     if ((a.n_max & 3) == 0) {
         *reinterpret_cast<f32x4 *>(dst) = v;
