@@ -69,6 +69,7 @@ __device__ int block_scan(int v, int &total, int *sScan)
 
 struct SelShared {
     uint32_t hist[2][kCopies * kHistStride];   // alternating: one is counted, the other cleared
+    int part[kSelectThreads / 256][256];       // per-bin sums over a quarter of the copies
     int scan[kWaves + 1];
     int bcast[2];
 };
@@ -76,11 +77,12 @@ struct SelShared {
 // Threshold of the `kth` largest eligible key (1 <= kth <= #eligible): returns the
 // threshold key and, in `need`, how many keys equal to it belong to the top kth.
 // Per 8-bit pass: every thread counts its keys into the current histogram (lane-slot
-// copies, one atomic per run of equal digits), one barrier, then wave 0 alone sums the copies, scans the bins from the top
-// with shuffles and picks the digit while the other waves clear the other histogram for
-// the next pass; one more barrier publishes the digit.  hist[0] must be zero on entry and
-// is zero again on return (the last pass counts into hist[1], which the next call's
-// first pass clears).
+// copies, one atomic per run of equal digits); barrier; every thread sums one bin over
+// a quarter of the copies and clears its share of the other histogram (for the next
+// pass); barrier; wave 0 adds the four quarters of its 4 bins per lane, scans the bins
+// from the top with shuffles and picks the digit; a last barrier publishes it.  hist[0]
+// must be zero on entry and is zero again on return (the last pass counts into hist[1],
+// which the next call's first pass clears).
 template <int E>
 __device__ uint32_t radix_select(const uint32_t (&key)[E], uint64_t elig, int kth, int &need,
                                  SelShared &sh)
@@ -117,6 +119,19 @@ __device__ uint32_t radix_select(const uint32_t (&key)[E], uint64_t elig, int kt
         if (run)
             atomicAdd(&hist[slot * kHistStride + cur], run);
         __syncthreads();
+        {
+            constexpr int kQ = kSelectThreads / 256;          // quarters of the copies
+            constexpr int kPerQ = kCopies / kQ;
+            const int bin = tid & 255, q = tid >> 8;
+            int v = 0;
+#pragma unroll
+            for (int cp = 0; cp < kPerQ; ++cp)
+                v += (int)hist[(q * kPerQ + cp) * kHistStride + bin];
+            sh.part[q][bin] = v;
+            for (int i = tid; i < kCopies * kHistStride; i += kSelectThreads)
+                other[i] = 0;
+        }
+        __syncthreads();
         if (tid < 64) {
             // lane holds bins 255-4l .. 252-4l (descending)
             int c[4], tot = 0;
@@ -124,9 +139,9 @@ __device__ uint32_t radix_select(const uint32_t (&key)[E], uint64_t elig, int kt
             for (int j = 0; j < 4; ++j) {
                 const int bin = 255 - 4 * lane - j;
                 int v = 0;
-#pragma unroll 8
-                for (int cp = 0; cp < kCopies; ++cp)
-                    v += (int)hist[cp * kHistStride + bin];
+#pragma unroll
+                for (int q = 0; q < kSelectThreads / 256; ++q)
+                    v += sh.part[q][bin];
                 c[j] = v;
                 tot += v;
             }
@@ -146,9 +161,6 @@ __device__ uint32_t radix_select(const uint32_t (&key)[E], uint64_t elig, int kt
                 }
                 before += c[j];
             }
-        } else {
-            for (int i = tid - 64; i < kCopies * kHistStride; i += kSelectThreads - 64)
-                other[i] = 0;
         }
         __syncthreads();
         prefix |= (uint32_t)sh.bcast[0] << shift;
