@@ -194,12 +194,11 @@ __device__ uint64_t take_top(const uint32_t (&key)[E], uint64_t elig, int kth, S
     return sel;
 }
 
-// The thread's E keys (positions base .. base+E-1 of one score row), masked by `valid`:
-// 16-byte loads when the row is 16-byte aligned and the range lies inside it, else
-// scalar loads at clamped positions.
+// The raw bits of the thread's E scores (positions base .. base+E-1 of one score row):
+// 16-byte loads when the row is 16-byte aligned and the range lies inside it, else scalar
+// loads at clamped positions (n_max >= 1).
 template <int E>
-__device__ __forceinline__ void load_keys(uint32_t (&key)[E], const float *row, int base, int n_max,
-                                          uint64_t valid)
+__device__ __forceinline__ void load_raw(uint32_t (&raw)[E], const float *row, int base, int n_max)
 {
     if ((n_max & 3) == 0 && base + E <= n_max) {
         const float4 *p = reinterpret_cast<const float4 *>(row + base);
@@ -209,19 +208,25 @@ __device__ __forceinline__ void load_keys(uint32_t (&key)[E], const float *row, 
             v[i] = p[i];
 #pragma unroll
         for (int i = 0; i < E / 4; ++i) {
-            key[4 * i] = ord_key(v[i].x);
-            key[4 * i + 1] = ord_key(v[i].y);
-            key[4 * i + 2] = ord_key(v[i].z);
-            key[4 * i + 3] = ord_key(v[i].w);
+            raw[4 * i] = __float_as_uint(v[i].x);
+            raw[4 * i + 1] = __float_as_uint(v[i].y);
+            raw[4 * i + 2] = __float_as_uint(v[i].z);
+            raw[4 * i + 3] = __float_as_uint(v[i].w);
         }
     } else {
 #pragma unroll
         for (int e = 0; e < E; ++e)
-            key[e] = ord_key(row[min(base + e, n_max - 1)]);
+            raw[e] = __float_as_uint(row[min(base + e, n_max - 1)]);
     }
+}
+
+// Raw score bits -> order-preserving keys, 0 outside `valid`.
+template <int E>
+__device__ __forceinline__ void to_keys(uint32_t (&key)[E], uint64_t valid)
+{
 #pragma unroll
     for (int e = 0; e < E; ++e)
-        key[e] = ((valid >> e) & 1) ? key[e] : 0u;
+        key[e] = ((valid >> e) & 1) ? ord_key(__uint_as_float(key[e])) : 0u;
 }
 
 template <int E>
@@ -230,22 +235,30 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
     __shared__ SelShared sh;
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const int N = clampi(a.ctx_len[b], 0, a.n_max);
-    const int k = clampi(a.budget[b], 0, min(N, a.k_max));
+    const int base = tid * E;
+    // the draft scores are requested first, before the sequence's arguments are known
+    uint32_t key[E];
+    if (a.score_draft && a.n_max > 0)
+        load_raw<E>(key, a.score_draft + (int64_t)b * a.n_max, base, a.n_max);
+    // every per-sequence argument in one round of loads
+    const int n_raw = a.ctx_len[b], k_raw = a.budget[b], s_raw = a.n_sink[b], w_raw = a.n_window[b];
+    const int m_raw = a.score_draft ? a.m[b] : 0;
+    const int N = clampi(n_raw, 0, a.n_max);
+    const int k = clampi(k_raw, 0, min(N, a.k_max));
     int32_t *out = a.idx + (int64_t)b * a.k_max;
     if (tid == 0)
         a.count[b] = k;
     if (k == N) {
         for (int i = tid; i < a.k_max; i += kSelectThreads)
             out[i] = i < N ? i : -1;
+        wait_vmcnt<0>();   // the early score loads
         return;
     }
-    const int s = clampi(a.n_sink[b], 0, k);
-    const int w = clampi(a.n_window[b], 0, k - s);
-    const int md = a.score_draft ? clampi(a.m[b], 0, k - s - w) : 0;
+    const int s = clampi(s_raw, 0, k);
+    const int w = clampi(w_raw, 0, k - s);
+    const int md = a.score_draft ? clampi(m_raw, 0, k - s - w) : 0;
     const int r = k - s - w - md;
 
-    const int base = tid * E;
     uint64_t valid = 0, prot = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -259,14 +272,14 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
     for (int i = tid; i < kCopies * kHistStride; i += kSelectThreads)
         sh.hist[0][i] = 0;
     __syncthreads();
-    uint32_t key[E];
     uint64_t selD = 0, selT = 0;
     if (md > 0) {
-        load_keys<E>(key, a.score_draft + (int64_t)b * a.n_max, base, a.n_max, valid);
+        to_keys<E>(key, valid);
         selD = take_top<E>(key, valid & ~prot, md, sh);
     }
     if (r > 0) {
-        load_keys<E>(key, a.score_target + (int64_t)b * a.n_max, base, a.n_max, valid);
+        load_raw<E>(key, a.score_target + (int64_t)b * a.n_max, base, a.n_max);
+        to_keys<E>(key, valid);
         selT = take_top<E>(key, valid & ~prot & ~selD, r, sh);
     }
     const uint64_t fin = prot | selD | selT;
