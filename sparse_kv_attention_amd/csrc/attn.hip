@@ -8,23 +8,27 @@
 // "Significance and Limitations" 2).
 //
 // Work decomposition (gfx950, 64-wide waves, 4 waves per workgroup):
-//   workgroup = (b, g, query group, split of the token list).  The split's list
-//   positions (at most 1024) are resolved once into an LDS table of tokens (and pages),
-//   then each wave streams its own 16-token tiles (tiles w, w+4, ...) with no workgroup
-//   barrier inside the loop:
-//     - K rows are loaded straight into the MFMA A-operand layout (lane = row, four
-//       16-byte loads per lane) and S^T = K Q^T is formed for all (up to QT*16) queries
-//       of the KV head's group on v_mfma_f32_16x16x32_bf16 (fp32 accumulate);
-//     - the wave's online softmax keeps P in registers: the S^T output layout of a lane
-//       (4 tokens x 1 query) is exactly the B operand of v_mfma_f32_16x16x16_bf16;
-//     - V rows are transposed through a wave-private LDS tile and O^T += V^T P^T is
-//       accumulated over the whole head dim;
-//     - the next tile's K and V loads are in flight while the current one is computed.
-//   The four waves merge their (max, sum, O) in LDS at the end; splits of one pair are
-//   merged by a second kernel with log-sum-exp weights in fixed split order (a kernel
-//   boundary, not per-workgroup device-scope fences, which write back and invalidate
-//   the XCD's L2).  Block ids are mapped so that all splits of one pair run on one XCD
-//   (blocks are dispatched round-robin over the 8 XCDs).
+//   workgroup = (b, g, query group, split of the selected positions).  The split's
+//   positions (at most 2048) are resolved once into an LDS table of 64-bit row offsets
+//   (page tables are looked up there), then each wave streams its own 32-position steps
+//   (steps w, w+4, ...) with no workgroup barrier inside the loop:
+//     - a step's K and V rows are moved into one of the wave's two LDS ring slots by LDS
+//       DMA (non-temporal; every 64-lane instruction moves whole rows), with 16-byte
+//       chunks XOR-swizzled per row so that the operand reads are bank-conflict free; a
+//       slot is refilled as soon as its operands are in registers;
+//     - S^T = K Q^T is formed for all (up to QT*16) queries of the KV head's group on
+//       v_mfma_f32_16x16x32_bf16 (fp32 accumulate); the S^T output layout of a lane is
+//       exactly the B operand of the PV product, so P never leaves registers;
+//     - V^T comes from transposing LDS reads (ds_read_b64_tr_b16) and O^T += V^T P^T is
+//       accumulated on 16x16x32 over the whole head dim; the online softmax is in base 2
+//       with a lazy rescale;
+//     - the new-token block (at most 16 rows, causal among themselves) is one 16-row
+//       step of wave 3 of the last split, loaded first into its own LDS area.
+//   The four waves merge their (max, sum, O) in one LDS exchange at the end; splits of
+//   one pair are merged by a second kernel with log-sum-exp weights in fixed split order
+//   (a kernel boundary, not per-workgroup device-scope fences, which write back and
+//   invalidate the XCD's L2).  Block ids are mapped so that all splits of one pair run
+//   on one XCD (blocks are dispatched round-robin over the 8 XCDs).
 #include "device.hpp"
 #include "launch.hpp"
 
