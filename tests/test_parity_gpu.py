@@ -120,6 +120,17 @@ def test_widest_verify_block():
     check_pipeline(W.make_inputs(w, device="cuda"), [0], [0], [0, 1])
 
 
+def test_scoring_three_tiles_per_workgroup():
+    # 8 sequences x 4 SRH groups per signal = 32 streams, so the softmax-mode logit grid has
+    # 16 workgroups per stream; 12288 tokens = 48 tiles of 256, i.e. three per workgroup:
+    # the two-tiles-in-flight loop ends on a half-used pair
+    w = Workload(name="odd_tiles", batch=8, n_ctx=12288, target=ModelShape(1, 16, 4, 128),
+                 draft=ModelShape(1, 8, 4, 64), gamma=4, budget=512, n_sink=16, n_window=64, m=192,
+                 srh_draft=((0, 0), (0, 2), (0, 4), (0, 6)), srh_target=((0, 0), (0, 4), (0, 8), (0, 12)),
+                 seed=17)
+    check_pipeline(W.make_inputs(w, device="cuda"), [0], [], [0, 5], b_score=[0, 3, 7])
+
+
 def test_query_groups_split():
     # G = 16 query heads per KV head x 8 verify queries = 128 rows: two query groups
     w = small("qgroups", 2, 400, 32, 2, 128, 7, 100, 4, 8, 20, seed=14)
