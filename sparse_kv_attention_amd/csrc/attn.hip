@@ -527,12 +527,11 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
 // Every (row, 4-column) item is one thread (D/64 blocks per 16-row tile); the per-split
 // maxima and sums of a row are read by all of its threads (cache hits), so there is a
 // single round of loads.
-template <int D, int QT>
+template <int D, int QT, int kPre>   // kPre: splits whose partials are fetched before any math
 __global__ __launch_bounds__(kThreads) void verify_attn_merge_kernel(AttnArgs a)
 {
     constexpr int QR = QT * 16;
     constexpr int BPQ = D / 64;       // blocks per 16-row query tile
-    constexpr int kPre = 8;           // splits whose partials are fetched before any math
     // blocks of a pair run on the XCD that ran its split workgroups (blockIdx % 8)
     const int x = blockIdx.x;
     const int hi = x >> 3;
@@ -603,7 +602,13 @@ hipError_t launch_qt(const AttnArgs &a, dim3 grid, hipStream_t st)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1)
         return e;
-    hipLaunchKernelGGL((verify_attn_merge_kernel<D, QT>), dim3((unsigned)((a.B * a.Hkv + 7) / 8 * 8 * a.qgroups * QT * (D / 64))), dim3(kThreads), 0, st, a);
+    const dim3 mgrid((unsigned)((a.B * a.Hkv + 7) / 8 * 8 * a.qgroups * QT * (D / 64)));
+    if (a.splits <= 4)
+        hipLaunchKernelGGL((verify_attn_merge_kernel<D, QT, 4>), mgrid, dim3(kThreads), 0, st, a);
+    else if (a.splits <= 8)
+        hipLaunchKernelGGL((verify_attn_merge_kernel<D, QT, 8>), mgrid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((verify_attn_merge_kernel<D, QT, 16>), mgrid, dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
