@@ -221,7 +221,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "dustin_sparse_verify_attn, one layer: verify_attn_split_kernel<128,3,2> "
-                               "+ verify_attn_merge_kernel<128,3>",
+                               "+ verify_attn_merge_kernel<128,3,4>",
                      "algorithmic_bytes_per_call": b_attn, "call_us": round(us_attn_call, 2)},
     }
 
