@@ -281,9 +281,7 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
     a.total_qheads = total_qheads;
     a.total_pairs = lay.total_pairs;
     a.n_tiles = lay.n_tiles;
-    // softmax-mode logit kernel: two resident workgroups per CU (its LDS and register use),
-    // each streaming a run of tiles, so the grid is one round
-    a.n_parts = std::max(1, std::min(lay.n_parts, (2 * device_cus() + n_groups * B - 1) / (n_groups * B)));
+    a.n_parts = lay.n_parts;   // the most the workspace holds; the launch picks its count
     a.ctx_clamp = ctx_clamp;
     a.ctx_len = ctx_len;
     a.q = static_cast<const uint16_t *>(q);
@@ -305,7 +303,7 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
         qh += sg.n_qheads;
         pr += sg.n_pairs;
     }
-    const hipError_t e = launch_score(a, head_dim, max_pairs, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_score(a, head_dim, max_pairs, device_cus(), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
 }
 

@@ -72,7 +72,8 @@ struct ScoreArgs {
     ScoreGroup grp[kMaxGroups];
 };
 
-hipError_t launch_score(const ScoreArgs &a, int head_dim, int max_pairs, hipStream_t st);
+// cus: compute units of the device (sizes the softmax-mode grid to one resident round)
+hipError_t launch_score(ScoreArgs a, int head_dim, int max_pairs, int cus, hipStream_t st);
 
 // ---------------------------------------------------------------- selection
 constexpr int kSelectThreads = 1024;

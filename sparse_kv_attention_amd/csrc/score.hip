@@ -98,6 +98,26 @@ __device__ __forceinline__ void wave_reduce_f32(float (&v)[N])
     }
 }
 
+// In-place max (MAX) or sum over each 16-lane row of N values per lane; every lane of a
+// row ends with its row's results.
+template <int N, bool MAX>
+__device__ __forceinline__ void row16_reduce_f32(float (&v)[N])
+{
+    auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = op(v[i], __uint_as_float(dpp32<0xB1>(__float_as_uint(v[i]))));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = op(v[i], __uint_as_float(dpp32<0x4E>(__float_as_uint(v[i]))));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = op(v[i], __uint_as_float(dpp32<0x141>(__float_as_uint(v[i]))));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = op(v[i], __uint_as_float(dpp32<0x140>(__float_as_uint(v[i]))));
+}
+
 __device__ __forceinline__ double wave_max_f64_dpp(double v)
 {
     v = fmax(v, dpp64<0xB1>(v));
@@ -124,6 +144,8 @@ __device__ __forceinline__ double quad_xor(double v)
 template <int D, int PC, bool FLAT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8 ? 1 : 2))) void srh_prob_logits_kernel(ScoreArgs a)
 {
+    // groups of 4 pairs: the dot products run on the fp64 matrix cores
+    constexpr bool MF = PC == 4;
     // lanes per token group = tokens per lane: 4 where registers allow (each query value
     // then feeds four tokens), 2 for the 128-wide rows (two tiles of them are in flight)
     constexpr int S = (D > 64 || PC > 8) ? 2 : 4;
@@ -322,6 +344,84 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
             runM = M1;
         }
     };
+
+    // Matrix-core path (groups of 4 pairs).  Block b (of 4) of v_mfma_f64_4x4x4f64 computes
+    // C[i][j] += sum_k A[i][k] B[k][j] with A[i][k] at lane 16k + 4b + i, B[k][j] at lane
+    // 16k + 4b + j and C[i][j] at lane 16i + 4b + j (lane layout measured on the GPU).
+    // Rows i are the pairs, columns j tokens, and step s covers the head-dim elements
+    // (D/4) k + s, the same order for Q and K; one instruction covers 16 tokens (4 blocks
+    // x 4), so a wave's 64 tokens are four accumulators.  Products of bf16 values are exact
+    // in fp64.  After the products, lane l holds pair l/16 of token l%16 of each 16-token
+    // group, so every per-pair reduction stays within a 16-lane row, and pair p keeps its
+    // running (max, sum) in lane 16p.  The fp64 matrix rate equals the vector rate on this
+    // part; the gain is in the query reads (one per 16 tokens) and the reduce-scatter that
+    // is no longer needed.  A fifth pair on the vector unit made 5-pair groups slower.
+    auto process_mf = [&](auto tile) {   // generic: only instantiated where it is called
+        __syncthreads();
+        constexpr int DK = D / 4;
+        const int kq = lane >> 4;
+        const int t16 = lane & 15;
+        const double *qa_row = &sQ[lane & 3][kq * DK];
+        const uint8_t *k_row = &sK[(64 * w + t16) * RSTR + kq * DK * 2];
+        double cm[4] = {0.0, 0.0, 0.0, 0.0};
+        // 8 head-dim elements (one 16-byte LDS read per token) at a time
+#pragma unroll 1
+        for (int c = 0; c < DK / 8; ++c) {
+            u32x4 kraw[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                kraw[g] = *reinterpret_cast<const u32x4 *>(k_row + 16 * g * RSTR + c * 16);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const double qa = qa_row[8 * c + s];
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint32_t wd = kraw[g][s / 2];
+                    const double kv = (double)((s & 1) ? bf16_hi(wd) : bf16_lo(wd));
+                    cm[g] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa, kv, cm[g], 0, 0, 0);
+                }
+            }
+        }
+        // statistics of the wave's 64 tokens (one statistics tile) per pair: the maximum of
+        // the fp32-rounded logits as the tile's reference, offsets against it, sum of exp2
+        const int stile = tile * (kProbTile / kStatTile) + w;
+        const int tok0 = tile * kProbTile + 64 * w + t16;      // + 16 g
+        const int pr = lane >> 4;                              // the lane's pair
+        double lm[4];
+        float red[1] = {-INFINITY};
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            lm[g] = tok0 + 16 * g < N ? cm[g] * a.mul : -INFINITY;
+            red[0] = fmaxf(red[0], (float)lm[g]);
+        }
+        row16_reduce_f32<1, true>(red);
+        const float mx = red[0];
+        float off[4];
+        red[0] = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const bool vld = tok0 + 16 * g < N;
+            off[g] = vld ? (float)(lm[g] - (double)mx) : -INFINITY;
+            red[0] += vld ? fast_exp2(off[g]) : 0.f;
+        }
+        row16_reduce_f32<1, false>(red);
+        const int64_t row0 = (int64_t)b * a.total_pairs + G.pair0;
+        if (pr < G.n_pairs) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                if (tok0 + 16 * g < N)
+                    a.logits[(row0 + pr) * a.n_pad + tok0 + 16 * g] = off[g];
+            if (t16 == 0 && stile < a.n_tiles)   // a wave past n_tiles holds no token
+                a.tile_max[(row0 + pr) * a.n_tiles + stile] = (double)mx;
+        }
+        if (mx > -INFINITY) {
+            const double m = (double)mx;
+            const double M1 = fmax(runM, m);
+            const double s0 = runM > -INFINITY ? runS * (double)fast_exp2((float)(runM - M1)) : 0.0;
+            runS = s0 + (double)red[0] * (double)fast_exp2((float)(m - M1));
+            runM = M1;
+        }
+    };
     const int step = gridDim.x;
     int tile = blockIdx.x;
     u32x4 krA[LPT];
@@ -336,26 +436,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
         for (int k = 0; k < pairs_of_tiles; ++k) {
             stage(krA);
             issue(krA, tile + 2 * step);
-            process(tile);
+            if constexpr (MF)
+                process_mf(tile);
+            else
+                process(tile);
             stage(krB);
             issue(krB, tile + 3 * step);
-            if (tile + step < n_live)
-                process(tile + step);
+            if (tile + step < n_live) {
+                if constexpr (MF)
+                    process_mf(tile + step);
+                else
+                    process(tile + step);
+            }
             tile += 2 * step;
         }
     } else {
         for (;;) {
             stage(krA);
             issue(krA, tile + step);
-            process(tile);
+            if constexpr (MF)
+                process_mf(tile);
+            else
+                process(tile);
             tile += step;
             if (tile >= n_live)
                 break;
         }
     }
-    if (lane < PC) {
-        sRunM[w][lane] = runM;
-        sRunS[w][lane] = runS;
+    {
+        // the lane holding pair p's running (max, sum): lane p, or lane 16p on the
+        // matrix-core path
+        const int p_own = !MF ? (lane < PC ? lane : -1) : ((lane & 15) == 0 ? lane >> 4 : -1);
+        if (p_own >= 0) {
+            sRunM[w][p_own] = runM;
+            sRunS[w][p_own] = runS;
+        }
     }
     __syncthreads();
     if (tid < G.n_pairs) {   // this workgroup's (max, sum) per pair, over its waves
@@ -577,46 +692,53 @@ hipError_t launch_logit_sum(const ScoreArgs &a, int pt, dim3 grid, hipStream_t s
     return hipGetLastError();
 }
 
-// the softmax-mode kernel, instantiated for the pair counts of one group
+// The softmax-mode kernel, instantiated for the pair counts of one group.  Its grid is one
+// resident round: as many workgroups per CU as the variant's registers and LDS allow (asked
+// of the runtime once per variant), each streaming a run of tiles.  a.n_parts comes in as
+// the workspace's maximum and leaves as the count launched (the finalize reads that many).
 template <int D>
-hipError_t launch_prob(const ScoreArgs &a, int max_pairs, dim3 grid, hipStream_t st)
+hipError_t launch_prob(ScoreArgs &a, int max_pairs, int cus, hipStream_t st)
 {
     bool flat = true;
     for (int g = 0; g < a.n_groups; ++g)
         flat = flat && !a.grp[g].k.pt && a.grp[g].k.st >= 0 && a.grp[g].k.st * 2 < (int64_t)1 << 32;
-#define DUSTIN_PROB(PCV)                                                                            \
-    do {                                                                                            \
-        if (flat)                                                                                   \
-            hipLaunchKernelGGL((srh_prob_logits_kernel<D, PCV, true>), grid, dim3(kThreads), 0, st, a);  \
-        else                                                                                        \
-            hipLaunchKernelGGL((srh_prob_logits_kernel<D, PCV, false>), grid, dim3(kThreads), 0, st, a); \
-    } while (0)
+    auto go = [&](auto kern) {
+        static const int per_cu = [&] {
+            int n = 0;
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kThreads, 0) != hipSuccess || n < 1)
+                n = 1;
+            return n;
+        }();
+        const int ws = a.n_groups * a.B;
+        a.n_parts = std::max(1, std::min(a.n_parts, (per_cu * cus + ws - 1) / ws));
+        const dim3 grid((unsigned)a.n_parts, (unsigned)a.n_groups, (unsigned)a.B);
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    };
+#define DUSTIN_PROB(PCV)                                                              \
+    return flat ? go(srh_prob_logits_kernel<D, PCV, true>) : go(srh_prob_logits_kernel<D, PCV, false>)
     if (max_pairs <= 4)
         DUSTIN_PROB(4);
-    else if (max_pairs <= 5)
+    if (max_pairs <= 5)
         DUSTIN_PROB(5);
-    else if (max_pairs <= 8)
+    if (max_pairs <= 8)
         DUSTIN_PROB(8);
-    else if (max_pairs <= 16)
+    if (max_pairs <= 16)
         DUSTIN_PROB(16);
-    else
-        return hipErrorInvalidValue;
 #undef DUSTIN_PROB
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_score(const ScoreArgs &a, int head_dim, int max_pairs, hipStream_t st)
+hipError_t launch_score(ScoreArgs a, int head_dim, int max_pairs, int cus, hipStream_t st)
 {
     hipError_t e = hipSuccess;
     if (a.mode == DUSTIN_SCORE_PROB_SUM) {
-        const dim3 g1((unsigned)a.n_parts, (unsigned)a.n_groups,
-                      (unsigned)a.B);
         if (head_dim == 64)
-            e = launch_prob<64>(a, max_pairs, g1, st);
+            e = launch_prob<64>(a, max_pairs, cus, st);
         else
-            e = launch_prob<128>(a, max_pairs, g1, st);
+            e = launch_prob<128>(a, max_pairs, cus, st);
         if (e != hipSuccess)
             return e;
     } else {
