@@ -32,15 +32,16 @@ static double dot_bf16(const uint16_t *a, const uint16_t *b, int d)
  * attention scores aggregated into one importance map) and Methodology 2 (only the SRHs
  * are scored).  The attention score of a context token under one (head, query) pair is
  * its softmax probability over the scored context; the map sums those probabilities.
- * LOGIT_SUM2 follows the German Vegas summary 2A (the objective sums raw logits over
- * queries and heads) restricted to the two queries of 2B (first draft token, bonus token).
+ * LOGIT_SUM_ALL is the objective of the German Vegas summary 2A as it stands: raw logits
+ * summed over every query and every head.  LOGIT_SUM2 restricts it to the two queries of
+ * 2B (first draft token, bonus token).
  * ---------------------------------------------------------------------------------- */
 int oracle_score_stream(int B, int n_rows, int n_max, const int32_t *ctx_len, int d,
                         const uint16_t *K, int n_heads, int n_q, const uint16_t *Q,
                         double scale, int mode, double *acc)
 {
     if (B < 0 || n_rows < 0 || n_max < 0 || d <= 0 || n_heads < 0 || n_q <= 0 || !ctx_len ||
-        !acc || (mode != ORACLE_PROB_SUM && mode != ORACLE_LOGIT_SUM2))
+        !acc || (mode != ORACLE_PROB_SUM && mode != ORACLE_LOGIT_SUM2 && mode != ORACLE_LOGIT_SUM_ALL))
         return -1;
     double *logit = (double *)malloc(sizeof(double) * (size_t)(n_max > 0 ? n_max : 1));
     if (!logit)
@@ -60,7 +61,7 @@ int oracle_score_stream(int B, int n_rows, int n_max, const int32_t *ctx_len, in
                 for (int i = 0; i < n; ++i)
                     logit[i] = scale * dot_bf16(q, Kb + (size_t)i * d, d);
                 double *out = acc + (size_t)b * n_max;
-                if (mode == ORACLE_LOGIT_SUM2) {
+                if (mode != ORACLE_PROB_SUM) {
                     for (int i = 0; i < n; ++i)
                         out[i] += logit[i];
                     continue;

@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-enum { ORACLE_PROB_SUM = 0, ORACLE_LOGIT_SUM2 = 1 };
+enum { ORACLE_PROB_SUM = 0, ORACLE_LOGIT_SUM2 = 1, ORACLE_LOGIT_SUM_ALL = 2 };
 
 /* Importance scores of one scored key stream, ADDED into acc[B][n_max].
  *   K   : [B][n_rows][d]      the stream's key rows (one head of one layer)
@@ -36,7 +36,8 @@ enum { ORACLE_PROB_SUM = 0, ORACLE_LOGIT_SUM2 = 1 };
  *   token i of sequence b is scored for 0 <= i < ctx_len[b] (<= n_rows, <= n_max)
  *   PROB_SUM   : for every (head, query) pair, softmax over i of scale*q.k_i, summed
  *   LOGIT_SUM2 : scale*q.k_i summed over heads and the queries {0, n_q-1} (query 0
- *                once when n_q == 1), no softmax                                     */
+ *                once when n_q == 1), no softmax
+ *   LOGIT_SUM_ALL : scale*q.k_i summed over heads and every query j < n_q, no softmax */
 int oracle_score_stream(int B, int n_rows, int n_max, const int32_t *ctx_len, int d,
                         const uint16_t *K, int n_heads, int n_q, const uint16_t *Q,
                         double scale, int mode, double *acc);

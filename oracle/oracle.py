@@ -14,7 +14,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
-PROB_SUM, LOGIT_SUM2 = 0, 1
+PROB_SUM, LOGIT_SUM2, LOGIT_SUM_ALL = 0, 1, 2
 
 _lib = None
 
@@ -34,8 +34,7 @@ def build(force: bool = False) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            build()
+        build()   # no-op unless the library is missing or older than its sources
         L = ctypes.CDLL(LIB_PATH)
         P = ctypes.c_void_p
         i = ctypes.c_int

@@ -112,3 +112,53 @@ def test_vegas_objective_argmax_is_topk():
                 best, best_set = v, T
         idx, cnt = O.select([n], None, acc, [k], [0], [0], [0], k)
         assert tuple(idx[0, :cnt[0]]) == tuple(sorted(best_set))
+
+
+def test_logit_sum_all_closed_form():
+    """The full Vegas aggregate (German Vegas summary 2A: raw logits summed over every
+    query and head) is linear in the queries: score_i = scale * (sum of all queries) . k_i,
+    one matrix-vector product with the summed query."""
+    rng = np.random.default_rng(7)
+    B, n, d, nh, nq = 2, 40, 16, 3, 5
+    K, Q = rand_stream(rng, B, n, d, nh, nq)
+    acc = O.score_stream(bits(K), bits(Q), [n, 17], n, 0.3, O.LOGIT_SUM_ALL)
+    for b, nb in ((0, n), (1, 17)):
+        qsum = Q[b].double().reshape(-1, d).sum(0).numpy()
+        ref = 0.3 * (K[b, :nb].double().numpy() @ qsum)
+        np.testing.assert_allclose(acc[b, :nb], ref, rtol=1e-12, atol=1e-12)
+        assert np.all(acc[b, nb:] == 0)
+
+
+def test_logit_sum_all_reduces_to_collect2_for_two_queries():
+    """With at most two queries the first and last query are all of them, so the full
+    aggregate and the Collect-2 restriction (2B) coincide."""
+    rng = np.random.default_rng(8)
+    for nq in (1, 2):
+        K, Q = rand_stream(rng, 2, 30, 8, 2, nq)
+        a = O.score_stream(bits(K), bits(Q), [30, 11], 30, 0.7, O.LOGIT_SUM_ALL)
+        b = O.score_stream(bits(K), bits(Q), [30, 11], 30, 0.7, O.LOGIT_SUM2)
+        np.testing.assert_array_equal(a, b)
+    # with more queries the middle ones count: the difference is their own logit sum
+    K, Q = rand_stream(rng, 1, 20, 8, 2, 4)
+    a = O.score_stream(bits(K), bits(Q), [20], 20, 1.0, O.LOGIT_SUM_ALL)
+    b = O.score_stream(bits(K), bits(Q), [20], 20, 1.0, O.LOGIT_SUM2)
+    mid = K[0].double().numpy() @ Q[0, :, 1:3].double().reshape(-1, 8).sum(0).numpy()
+    np.testing.assert_allclose(a[0] - b[0], mid, rtol=1e-12, atol=1e-12)
+
+
+def test_vegas_full_objective_argmax_is_topk():
+    """Brute force over all size-k subsets of the objective summed over every query and
+    head equals the oracle's pure top-k on the LOGIT_SUM_ALL score."""
+    rng = np.random.default_rng(9)
+    for trial in range(6):
+        n, d, nh, nq, k = 12, 8, 2, 5, 4
+        K, Q = rand_stream(rng, 1, n, d, nh, nq)
+        acc = O.score_stream(bits(K), bits(Q), [n], n, 0.5, O.LOGIT_SUM_ALL)
+        L = np.einsum("hqd,nd->hqn", Q[0].double().numpy(), K[0].double().numpy()) * 0.5
+        best, best_set = -np.inf, None
+        for T in itertools.combinations(range(n), k):
+            v = sum(L[h, t, i] for t in range(nq) for h in range(nh) for i in T)
+            if v > best + 1e-12:
+                best, best_set = v, T
+        idx, cnt = O.select([n], None, acc, [k], [0], [0], [0], k)
+        assert tuple(idx[0, :cnt[0]]) == tuple(sorted(best_set))
