@@ -178,6 +178,19 @@ def main():
     us_attn_all = timed(lambda: [step.attn(l) for l in attn_layers], reps)
     dl = attn_layers[: max(1, min(args.dense_layers, len(attn_layers)))]
     us_dense_layer = timed(lambda: [step.dense(l) for l in dl], 3) / len(dl)
+    # Vegas-style target signal on the same streams (raw logits summed over the first and
+    # bonus queries, or over every query) and its pure top-k selection: not part of the step
+    variants = {}
+    for name, kw in (("vegas_collect2", {"logit_sum2": True}), ("vegas_all_queries", {"logit_sum_all": True})):
+        vs = SparseVerifyStep(inp, layers=attn_layers[:1], **kw)
+        vs.score()
+        vs.select()
+        us_v = timed(vs.score, reps)
+        variants[name] = {"score_us": round(us_v, 2),
+                          "score_gbs": round(score_bytes(B, inp.n_max, [T.d] * len(inp.target_groups), 1)
+                                             / (us_v * 1e-6) / 1e9, 1),
+                          "topk_select_us": round(timed(vs.select, reps), 2)}
+        del vs
 
     # ---- bytes ----
     n_ctx = inp.n_max
@@ -215,6 +228,7 @@ def main():
         "bytes": {"step": b_step, "attn_per_launch": b_attn, "score": b_score, "select": b_select},
         "score_gbs": round(b_score / (us_score * 1e-6) / 1e9, 1),
         "dense_attn_per_layer_us": round(us_dense_layer, 2),
+        "target_signal_variants": variants,
         "dense_attn_gbs": round(b_dense / (us_dense_layer * 1e-6) / 1e9, 1),
         "attn_speedup_vs_dense": round(us_dense_layer / us_attn_call, 2),
         "wall_s_timed": round(wall, 3),

@@ -53,7 +53,11 @@ enum {
     /* Sum over the SRH query heads and over the queries {0, n_q-1} of the scaled
        pre-softmax logit (German Vegas summary, 2A formula restricted to the first and
        the bonus query of 2B, "Collect-2-Query").  Query 0 counts once when n_q == 1.  */
-    DUSTIN_SCORE_LOGIT_SUM2 = 1
+    DUSTIN_SCORE_LOGIT_SUM2 = 1,
+    /* Sum over the SRH query heads and over every query j < n_q of the scaled
+       pre-softmax logit (German Vegas summary, 2A formula as stated: the aggregate over
+       all queries and heads).  Equal to LOGIT_SUM2 when n_q <= 2.                     */
+    DUSTIN_SCORE_LOGIT_SUM_ALL = 2
 };
 
 /* A bf16 K or V cache of one layer, contiguous or paged.
@@ -96,13 +100,14 @@ const char *dustin_status_string(dustin_status s);
  *                            softmax_i(scale * q[b][h][j] . K_g[b][i])
  *   LOGIT_SUM2 score[b][i] = sum over groups, heads, j in {0, n_q-1} of
  *                            scale * q[b][h][j] . K_g[b][i]
+ *   LOGIT_SUM_ALL           the same sum over every j < n_q
  * score[b][i] = 0 for ctx_len[b] <= i < n_max.  One call scores one signal (the draft
  * lookahead queries, or the target-historical queries); the softmax runs over the
  * committed context [0, ctx_len[b]).
  *   groups : (host) [n_groups], 1 <= n_groups <= 16; all groups share head_dim
  *   q      : bf16 [B][sum of n_qheads][n_q][head_dim], heads in group order
  *   head_dim in {64, 128}; 1 <= n_q <= 16; pairs per group (n_qheads * queries used)
- *   at most 16 in PROB_SUM mode and 64 in LOGIT_SUM2 mode
+ *   at most 16 in PROB_SUM mode and 64 in the logit-sum modes
  *   score  : fp32 [B][n_max], fully written
  *   workspace: at least dustin_srh_score_workspace_size(...) bytes, any contents
  * ------------------------------------------------------------------------------- */

@@ -186,11 +186,16 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
 }
 
 struct ScoreWs {
-    int n_pad, n_tiles, n_parts, total_pairs;
+    int n_pad, n_tiles, n_parts, total_pairs, logit_rows;
     size_t logits_off, max_off, pmax_off, psum_off, bytes;
 };
 
-int pairs_per_qhead(int n_q, int mode) { return mode == DUSTIN_SCORE_PROB_SUM ? n_q : std::min(2, n_q); }
+int pairs_per_qhead(int n_q, int mode) { return mode == DUSTIN_SCORE_LOGIT_SUM2 ? std::min(2, n_q) : n_q; }
+
+bool score_mode_ok(int mode)
+{
+    return mode == DUSTIN_SCORE_PROB_SUM || mode == DUSTIN_SCORE_LOGIT_SUM2 || mode == DUSTIN_SCORE_LOGIT_SUM_ALL;
+}
 
 ScoreWs score_workspace(int B, int n_max, int total_qheads, int n_q, int mode)
 {
@@ -202,10 +207,12 @@ ScoreWs score_workspace(int B, int n_max, int total_qheads, int n_q, int mode)
     w.n_parts = std::min(kScoreParts, n_ld);
     w.total_pairs = total_qheads * pairs_per_qhead(n_q, mode);
     const bool prob = mode == DUSTIN_SCORE_PROB_SUM;
+    // logit-sum modes keep one row per group (a group has at least one query head)
+    w.logit_rows = prob ? w.total_pairs : total_qheads;
     const size_t stats = prob ? (size_t)B * w.total_pairs * w.n_tiles : 0;
     const size_t parts = prob ? (size_t)B * w.total_pairs * w.n_parts : 0;
     w.logits_off = 0;
-    w.max_off = align_up(sizeof(float) * (size_t)B * w.total_pairs * w.n_pad);
+    w.max_off = align_up(sizeof(float) * (size_t)B * w.logit_rows * w.n_pad);
     w.pmax_off = w.max_off + align_up(sizeof(double) * stats);
     w.psum_off = w.pmax_off + align_up(sizeof(double) * parts);
     w.bytes = w.psum_off + align_up(sizeof(double) * parts);
@@ -231,8 +238,7 @@ const char *dustin_status_string(dustin_status s)
 dustin_status dustin_srh_score_workspace_size(int B, int n_max, int total_qheads, int n_q, int mode,
                                               size_t *bytes)
 {
-    if (!bytes || B < 0 || n_max < 0 || total_qheads < 0 || n_q <= 0 || n_q > 16 ||
-        (mode != DUSTIN_SCORE_PROB_SUM && mode != DUSTIN_SCORE_LOGIT_SUM2))
+    if (!bytes || B < 0 || n_max < 0 || total_qheads < 0 || n_q <= 0 || n_q > 16 || !score_mode_ok(mode))
         return DUSTIN_ERR_INVALID_ARG;
     *bytes = score_workspace(B, n_max, total_qheads, n_q, mode).bytes;
     return DUSTIN_OK;
@@ -245,7 +251,7 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
 {
     if (B < 0 || n_max < 0 || n_q <= 0 || !(scale == scale))
         return DUSTIN_ERR_INVALID_ARG;
-    if (mode != DUSTIN_SCORE_PROB_SUM && mode != DUSTIN_SCORE_LOGIT_SUM2)
+    if (!score_mode_ok(mode))
         return DUSTIN_ERR_INVALID_ARG;
     if (n_groups < 1 || !groups)
         return DUSTIN_ERR_INVALID_ARG;
@@ -280,6 +286,7 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
     a.mode = mode;
     a.total_qheads = total_qheads;
     a.total_pairs = lay.total_pairs;
+    a.logit_rows = mode == DUSTIN_SCORE_PROB_SUM ? lay.total_pairs : n_groups;
     a.n_tiles = lay.n_tiles;
     a.n_parts = lay.n_parts;   // the most the workspace holds; the launch picks its count
     a.ctx_clamp = ctx_clamp;

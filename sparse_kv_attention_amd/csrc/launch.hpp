@@ -61,10 +61,12 @@ struct ScoreGroup {
 
 struct ScoreArgs {
     int B, n_max, n_pad, n_groups, n_q, mode, total_qheads, total_pairs, n_tiles, n_parts, ctx_clamp;
+    int logit_rows;          // rows per sequence of `logits`: total_pairs (PROB_SUM), n_groups
     const int32_t *ctx_len;
     const uint16_t *q;
     double mul;              // PROB_SUM: scale*log2(e) (base-2 logits); LOGIT_SUM2: scale
-    float *logits;           // [B][total_pairs][n_pad]: PROB_SUM l - tile max; LOGIT_SUM2 l
+    float *logits;           // [B][logit_rows][n_pad]: PROB_SUM l - tile max per pair; logit-sum
+                             //   modes: per group, the sum of its pairs' logits
     double *tile_max;        // PROB_SUM: [B][total_pairs][n_tiles], n_tiles = ceil(n_max / kStatTile)
     double *part_max;        // PROB_SUM: [B][total_pairs][n_parts], one (max, sum of exp2(l - max))
     double *part_sum;        //   per workgroup of the logit kernel

@@ -22,9 +22,10 @@
 //                    and 1/Z from the workgroup partials (one wave per pair, loads of
 //                    several pairs in flight together), then per token the sum over pairs
 //                    of exp2(offset + tile max - max) / Z.
-// Logit-sum mode (LOGIT_SUM2): srh_logit_sum computes the raw scaled logits on MFMA (bf16
-// in, fp32 accumulate; the sum's tolerance scales with the sum of |logits|), and the
-// finalize kernel sums them per token.
+// Logit-sum modes (LOGIT_SUM2: queries 0 and n_q-1; LOGIT_SUM_ALL: every query):
+// srh_logit_sum computes the raw scaled logits on MFMA (bf16 in, fp32 accumulate; the
+// sum's tolerance scales with the sum of |logits|), adds a group's pairs in registers and
+// writes one row per group; the finalize kernel sums the groups per token.
 // Every pass streams: the K stream is read once, the logit workspace written once and
 // read once.
 #include "device.hpp"
@@ -512,7 +513,10 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
     const int t0 = tile * kSumTile;
     if (t0 >= N)
         return;
-    const int nqe = min(2, a.n_q);
+    // pair p of the group = (query head p / nqe, query p % nqe); LOGIT_SUM2 maps the
+    // second query slot to the last query
+    const bool all_q = a.mode == DUSTIN_SCORE_LOGIT_SUM_ALL;
+    const int nqe = all_q ? a.n_q : min(2, a.n_q);
     const float mul = (float)a.mul;
 
     // SRH queries as the MFMA B operand: lane holds pair pt*16 + li, its quarter of d
@@ -522,7 +526,8 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
         const int p = pt * 16 + li;
         if (p < G.n_pairs) {
             const int hl = p / nqe;
-            const int j = (p - hl * nqe) == 0 ? 0 : a.n_q - 1;
+            const int jj = p - hl * nqe;
+            const int j = all_q || jj == 0 ? jj : a.n_q - 1;
             const uint16_t *qp =
                 a.q + ((int64_t)(b * a.total_qheads + G.q_head0 + hl) * a.n_q + j) * D + quad * (D / 4);
 #pragma unroll
@@ -554,24 +559,29 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int tb = wbase + (bt + u) * 16 + 4 * quad;   // lane's 4 tokens
+            // column li of the product is pair pt*16 + li (zero queries past n_pairs): the
+            // group's sum over pairs is a sum over the 16 lanes of the lane's row
+            float c[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) {
-                f32x4 c{0.f, 0.f, 0.f, 0.f};
+                f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    c = mfma_bf16(kop[u][ks], qop[pt][ks], c);
-                c *= mul;
-                const int p = pt * 16 + li;
-                if (p < G.n_pairs && tb < N) {
-                    float *dst = a.logits + ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_pad + tb;
-                    if (tb + 3 < N) {
-                        *reinterpret_cast<f32x4 *>(dst) = c;
-                    } else {
+                    acc = mfma_bf16(kop[u][ks], qop[pt][ks], acc);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (tb + r < N)
-                                dst[r] = c[r];
-                    }
+                for (int r = 0; r < 4; ++r)
+                    c[r] += acc[r] * mul;
+            }
+            row16_reduce_f32<4, false>(c);
+            if (li == 0 && tb < N) {
+                float *dst = a.logits + ((int64_t)b * a.logit_rows + blockIdx.y) * a.n_pad + tb;
+                if (tb + 3 < N) {
+                    *reinterpret_cast<f32x4 *>(dst) = f32x4{c[0], c[1], c[2], c[3]};
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (tb + r < N)
+                            dst[r] = c[r];
                 }
             }
         }
@@ -594,10 +604,10 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
     const int tile0 = blockIdx.x * kFinTiles;
     // this thread's 4 tokens: the logits of the first kFinChunk pairs are requested before
     // the statistics (which do not need them), all in one round of loads
-    const int P = a.total_pairs;
+    const int P = prob ? a.total_pairs : a.n_groups;   // logit rows summed per token
     const int tb = blockIdx.x * kFinTokens + tid * 4;
     const bool live = tb < N;
-    const float *lg = a.logits + (int64_t)b * P * a.n_pad + tb;
+    const float *lg = a.logits + (int64_t)b * a.logit_rows * a.n_pad + tb;
     f32x4 lv[kFinChunk];
     auto fetch = [&](int p0) {
 #pragma unroll

@@ -17,7 +17,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdustin.so")
 
 OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4
-SCORE_PROB_SUM, SCORE_LOGIT_SUM2 = 0, 1
+SCORE_PROB_SUM, SCORE_LOGIT_SUM2, SCORE_LOGIT_SUM_ALL = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "

@@ -18,7 +18,11 @@ from .workloads import Inputs
 
 
 class SparseVerifyStep:
-    def __init__(self, inp: Inputs, layers: Optional[Sequence[int]] = None, logit_sum2: bool = False):
+    def __init__(self, inp: Inputs, layers: Optional[Sequence[int]] = None, logit_sum2: bool = False,
+                 logit_sum_all: bool = False):
+        """logit_sum2 / logit_sum_all: the Vegas-style target signal (German Vegas summary
+        2A/2B: raw logits summed over the first and bonus queries, or over every query)
+        with pure top-k selection and no draft signal."""
         self.inp = inp
         w = inp.w
         dev = inp.ctx_len.device
@@ -26,6 +30,7 @@ class SparseVerifyStep:
         self.B, self.n_max, self.k_max = w.batch, inp.n_max, inp.k_max
         self.T, self.Dm = w.target, w.draft
         self.layers = sorted(inp.k_cache) if layers is None else list(layers)
+        logit_sum2 = logit_sum2 or logit_sum_all
         self.logit_sum2 = logit_sum2
         # a draft signal exists only if the draft speculated at least one token
         self.has_draft = w.gamma > 0 and not logit_sum2
@@ -40,7 +45,8 @@ class SparseVerifyStep:
         self.score_target = torch.zeros((B, n_max), dtype=torch.float32, device=dev)
         nd = inp.q_srh_draft.shape[1]
         nt = inp.q_srh_target.shape[1]
-        mode_t = D.SCORE_LOGIT_SUM2 if logit_sum2 else D.SCORE_PROB_SUM
+        mode_t = (D.SCORE_LOGIT_SUM_ALL if logit_sum_all else
+                  D.SCORE_LOGIT_SUM2 if logit_sum2 else D.SCORE_PROB_SUM)
         self.mode_t = mode_t
         ws_score = D.dustin_srh_score_workspace_size(B, n_max, nt, w.n_verify, mode_t)
         if self.has_draft:

@@ -54,8 +54,9 @@ def oracle_scores(inp: Inputs, signal: str, mode: int, bsel):
     return acc
 
 
-def logit_abs_sum(inp: Inputs, signal: str, bsel):
-    """sum over (head, query in {0, last}) of |logit|: the conditioning of a logit sum."""
+def logit_abs_sum(inp: Inputs, signal: str, bsel, all_queries=False):
+    """sum over (head, query in {0, last} or every query) of |logit|: the conditioning of
+    a logit sum."""
     groups, q, caches, scale = signal_spec(inp, signal)
     out = np.zeros((len(bsel), inp.n_max))
     qoff = 0
@@ -63,7 +64,8 @@ def logit_abs_sum(inp: Inputs, signal: str, bsel):
         nq = len(g.qheads)
         for i, b in enumerate(bsel):
             K = rows(inp, caches[g.layer], b, inp.n_max)[:, g.kv_head].double().cpu()
-            Qs = q[b, qoff:qoff + nq][:, [0, q.shape[2] - 1]].double().cpu().reshape(-1, q.shape[-1])
+            js = list(range(q.shape[2])) if all_queries else [0, q.shape[2] - 1]
+            Qs = q[b, qoff:qoff + nq][:, js].double().cpu().reshape(-1, q.shape[-1])
             out[i] += (K @ Qs.T).abs().sum(1).numpy() * scale
         qoff += nq
     return out

@@ -19,24 +19,28 @@ from sparse_kv_attention_amd.workloads import ModelShape, Workload
 pytestmark = pytest.mark.gpu
 
 
-def step_for(inp, layers, logit_sum2=False):
+def step_for(inp, layers, logit_sum2=False, logit_sum_all=False):
     from sparse_kv_attention_amd.pipeline import SparseVerifyStep
-    return SparseVerifyStep(inp, layers=layers, logit_sum2=logit_sum2)
+    return SparseVerifyStep(inp, layers=layers, logit_sum2=logit_sum2, logit_sum_all=logit_sum_all)
 
 
-def check_pipeline(inp, attn_layers, dense_layers, b_attn, b_score=None, logit_sum2=False, b_dense=None):
+def check_pipeline(inp, attn_layers, dense_layers, b_attn, b_score=None, logit_sum2=False, b_dense=None,
+                   logit_sum_all=False):
     w = inp.w
     B = w.batch
     b_score = list(range(B)) if b_score is None else b_score
-    step = step_for(inp, attn_layers, logit_sum2)
+    step = step_for(inp, attn_layers, logit_sum2, logit_sum_all)
+    logit_sum2 = logit_sum2 or logit_sum_all
     say(f"[{w.name}] scoring")
     step.score()
     torch.cuda.synchronize()
     sd = step.score_draft.cpu().numpy()
     st = step.score_target.cpu().numpy()
     if logit_sum2:
-        ora = oracle_scores(inp, "target", O.LOGIT_SUM2, b_score)
-        check_scores(st[b_score], ora, "target logit-sum scores", cond=logit_abs_sum(inp, "target", b_score))
+        mode = O.LOGIT_SUM_ALL if logit_sum_all else O.LOGIT_SUM2
+        ora = oracle_scores(inp, "target", mode, b_score)
+        check_scores(st[b_score], ora, "target logit-sum scores",
+                     cond=logit_abs_sum(inp, "target", b_score, all_queries=logit_sum_all))
     else:
         if step.has_draft:
             check_scores(sd[b_score], oracle_scores(inp, "draft", O.PROB_SUM, b_score), "draft scores")
@@ -200,6 +204,15 @@ def test_logit_sum2_pure_topk():
     w = W.shrink(w, srh_target=((0, 0), (0, 1), (0, 4), (0, 8)))
     inp = W.make_inputs(w, device="cuda")
     check_pipeline(inp, [0], [], [0, 1, 2], logit_sum2=True)
+
+
+def test_logit_sum_all_pure_topk():
+    """The full Vegas aggregate over every query: one group of 4 query heads x 9 queries
+    (36 pairs, three 16-pair MFMA tiles) and one of 9 pairs, ragged tail of 2000 tokens."""
+    w = small("logitall", 3, 2000, 16, 4, 128, 8, 125, 0, 0, 0, seed=19)
+    w = W.shrink(w, srh_target=((0, 0), (0, 1), (0, 2), (0, 3), (0, 4)))
+    inp = W.make_inputs(w, device="cuda")
+    check_pipeline(inp, [0], [], [0, 2], logit_sum_all=True)
 
 
 def _paged_copy(x: torch.Tensor, page_size: int, seed: int):

@@ -54,3 +54,8 @@ def test_ragged_paged_hybrid(paged):
 def test_ragged_paged_logit_sum2_topk(paged):
     ctx = paged.ctx_len.cpu().numpy()
     check_pipeline(paged, [0], [], b_attn=[int(np.argmax(ctx))], b_score=[0, 7, 15], logit_sum2=True)
+
+
+def test_ragged_paged_logit_sum_all_topk(paged):
+    ctx = paged.ctx_len.cpu().numpy()
+    check_pipeline(paged, [0], [], b_attn=[int(np.argmin(ctx))], b_score=[1, 8, 14], logit_sum_all=True)
