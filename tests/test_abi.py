@@ -103,6 +103,9 @@ def test_workspace_queries():
     assert D._select_ws(8, 32768, ctypes.byref(n)) == D.OK
     assert D._score_ws(8, 32768, 4, 5, D.SCORE_PROB_SUM, ctypes.byref(n)) == D.OK
     assert n.value >= 8 * 20 * 32768 * 4
+    assert D._score_ws(8, 32768, 4, 5, D.SCORE_LOGIT_SUM_ALL, ctypes.byref(n)) == D.OK
+    assert n.value >= 8 * 4 * 32768 * 4         # one logit row per group (a group has >= 1 head)
+    assert D._score_ws(8, 32768, 4, 5, 3, ctypes.byref(n)) == D.ERR_INVALID_ARG
     assert D._score_ws(8, 32768, 4, 5, 7, ctypes.byref(n)) == D.ERR_INVALID_ARG
     assert D._score_ws(8, 32768, 4, 0, 0, ctypes.byref(n)) == D.ERR_INVALID_ARG
 
@@ -137,6 +140,9 @@ def test_score_rejects():
     assert f(ng=1, g=big) == D.ERR_UNSUPPORTED
     big[0].n_qheads = 33          # 33 heads x 2 queries = 66 logit-sum pairs > 64
     assert f(ng=1, g=big, mode=1) == D.ERR_UNSUPPORTED
+    big[0].n_qheads = 13          # 13 heads x 5 queries = 65 pairs over every query > 64
+    assert f(ng=1, g=big, mode=D.SCORE_LOGIT_SUM_ALL) == D.ERR_UNSUPPORTED
+    assert f(mode=3) == D.ERR_INVALID_ARG
 
 
 def test_select_rejects():
