@@ -273,3 +273,114 @@ int oracle_verify_attn(int B, int Hq, int Hkv, int d, int n_verify,
     free(acc);
     return rc;
 }
+
+/* ------------------------------------------------------------------------------------
+ * Attention recovery.  The English Dustin summary ("Methodology" 2) picks its SRHs by an
+ * Attention Recovery Rate that it names but does not define; the plain reading taken
+ * here is the share of the full-cache attention probability that the kept set carries.
+ * For every (b, h, t): the dense probabilities over [0, N) and the new tokens 0..t, then
+ * their sum over I_b and the new tokens (which both attentions see).
+ * ---------------------------------------------------------------------------------- */
+int oracle_attn_recovery(int B, int Hq, int Hkv, int d, int n_verify,
+                         const uint16_t *Q, const uint16_t *K, int n_cap,
+                         const int32_t *ctx_len, const int32_t *idx, const int32_t *count,
+                         int k_max, double scale, double *rec)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || d <= 0 || n_verify <= 0 || !Q || !K ||
+        !ctx_len || !idx || !count || !rec || k_max < 0 || n_cap < n_verify)
+        return -1;
+    int G = Hq / Hkv;
+    double *s = (double *)malloc(sizeof(double) * (size_t)n_cap);
+    unsigned char *kept = (unsigned char *)malloc((size_t)n_cap);
+    if (!s || !kept) {
+        free(s);
+        free(kept);
+        return -2;
+    }
+    int rc = 0;
+    for (int b = 0; b < B && !rc; ++b) {
+        int N = ctx_len[b];
+        int n_sel = count[b];
+        if (N < 0 || N + n_verify > n_cap || n_sel < 0 || n_sel > k_max) {
+            rc = -1;
+            break;
+        }
+        memset(kept, 0, (size_t)n_cap);
+        for (int j = 0; j < n_sel; ++j) {
+            int x = idx[(size_t)b * k_max + j];
+            if (x < 0 || x >= N) {
+                rc = -1;
+                break;
+            }
+            kept[x] = 1;
+        }
+        if (rc)
+            break;
+        for (int t = 0; t < n_verify; ++t) {
+            int n_all = N + t + 1; /* the context, then the new tokens 0..t */
+            for (int h = 0; h < Hq; ++h) {
+                int g = h / G;
+                const uint16_t *q = Q + (((size_t)b * n_verify + t) * Hq + h) * d;
+                double mx = -INFINITY;
+                for (int x = 0; x < n_all; ++x) {
+                    s[x] = scale * dot_bf16(q, K + (((size_t)b * n_cap + x) * Hkv + g) * d, d);
+                    if (s[x] > mx)
+                        mx = s[x];
+                }
+                double z = 0.0, kz = 0.0;
+                for (int x = 0; x < n_all; ++x) {
+                    double p = exp(s[x] - mx);
+                    z += p;
+                    if (x >= N || kept[x])
+                        kz += p;
+                }
+                rec[((size_t)b * Hq + h) * n_verify + t] = kz / z;
+            }
+        }
+    }
+    free(s);
+    free(kept);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------------------
+ * KV block write and commit.  English Dustin summary, Verification Workflow step 5:
+ * accepted tokens are appended to the cache and rejected ones discarded.  The block
+ * being verified is stored behind the committed context (where step 4 reads the new
+ * tokens); the commit then advances the context over the rows that are kept.  The block's
+ * first row is the token produced by the previous step and is always kept; each accepted
+ * draft token keeps one more row.  Rows behind the new context length are discarded
+ * (the next block overwrites them).
+ * ---------------------------------------------------------------------------------- */
+int oracle_kv_write_block(int B, int Hkv, int d, int n_new, const uint16_t *Knew,
+                          const uint16_t *Vnew, const int32_t *ctx_len, uint16_t *K,
+                          uint16_t *V, int n_cap)
+{
+    if (B < 0 || Hkv <= 0 || d <= 0 || n_new < 0 || !Knew || !Vnew || !ctx_len || !K || !V)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (ctx_len[b] < 0 || ctx_len[b] + n_new > n_cap)
+            return -1;
+    for (int b = 0; b < B; ++b)
+        for (int j = 0; j < n_new; ++j)
+            for (int g = 0; g < Hkv; ++g)
+                for (int e = 0; e < d; ++e) {
+                    size_t src = (((size_t)b * n_new + j) * Hkv + g) * d + e;
+                    size_t dst = (((size_t)b * n_cap + ctx_len[b] + j) * Hkv + g) * d + e;
+                    K[dst] = Knew[src];
+                    V[dst] = Vnew[src];
+                }
+    return 0;
+}
+
+int oracle_kv_commit(int B, int n_new, const int32_t *n_accept, int32_t *ctx_len)
+{
+    if (B < 0 || n_new <= 0 || !n_accept || !ctx_len)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        if (n_accept[b] < 0 || n_accept[b] > n_new - 1 || ctx_len[b] < 0)
+            return -1;
+    for (int b = 0; b < B; ++b)
+        ctx_len[b] += 1 + n_accept[b];
+    return 0;
+}

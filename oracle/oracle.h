@@ -64,6 +64,28 @@ int oracle_verify_attn(int B, int Hq, int Hkv, int d, int n_verify,
                        const int32_t *ctx_len, const int32_t *idx, const int32_t *count,
                        int k_max, double scale, double *O, double *lse);
 
+/* Attention recovery: the share of full-cache attention probability that falls on the
+ * kept set.  For (b, h, t) the dense softmax runs over [0, ctx_len[b]) and the new tokens
+ * 0..t; rec[b][h][t] is its sum over I_b (idx[b][0..count[b])) and the new tokens 0..t.
+ *   Q : [B][n_verify][Hq][d];  K : [B][n_cap][Hkv][d];  rec : [B][Hq][n_verify] out     */
+int oracle_attn_recovery(int B, int Hq, int Hkv, int d, int n_verify,
+                         const uint16_t *Q, const uint16_t *K, int n_cap,
+                         const int32_t *ctx_len, const int32_t *idx, const int32_t *count,
+                         int k_max, double scale, double *rec);
+
+/* The block of n_new tokens being verified, written into the caches behind the
+ * committed context: row ctx_len[b] + j of K and V (all heads) <- row j of Knew / Vnew.
+ * Nothing else changes and ctx_len is not advanced.
+ *   Knew, Vnew : [B][n_new][Hkv][d];  K, V : [B][n_cap][Hkv][d] (in/out)                */
+int oracle_kv_write_block(int B, int Hkv, int d, int n_new, const uint16_t *Knew,
+                          const uint16_t *Vnew, const int32_t *ctx_len, uint16_t *K,
+                          uint16_t *V, int n_cap);
+
+/* Commit after verification: the block's first row and its first n_accept[b] draft rows
+ * are kept, the rest are discarded.  ctx_len[b] += 1 + n_accept[b] (in/out),
+ * 0 <= n_accept[b] <= n_new - 1.                                                        */
+int oracle_kv_commit(int B, int n_new, const int32_t *n_accept, int32_t *ctx_len);
+
 #ifdef __cplusplus
 }
 #endif

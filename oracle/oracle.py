@@ -42,7 +42,11 @@ def lib():
         L.oracle_select.argtypes = [i, i, P, P, P, P, P, P, P, i, P, P]
         L.oracle_verify_attn.argtypes = [i, i, i, i, i, P, P, P, i, P, P, P, i,
                                          ctypes.c_double, P, P]
-        for f in (L.oracle_score_stream, L.oracle_select, L.oracle_verify_attn):
+        L.oracle_attn_recovery.argtypes = [i, i, i, i, i, P, P, i, P, P, P, i, ctypes.c_double, P]
+        L.oracle_kv_write_block.argtypes = [i, i, i, i, P, P, P, P, P, i]
+        L.oracle_kv_commit.argtypes = [i, i, P, P]
+        for f in (L.oracle_score_stream, L.oracle_select, L.oracle_verify_attn, L.oracle_attn_recovery,
+                  L.oracle_kv_write_block, L.oracle_kv_commit):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -113,3 +117,43 @@ def verify_attn(Q, K, V, ctx_len, idx, count, scale, Hkv):
     if rc:
         raise ValueError(f"oracle_verify_attn rc={rc}")
     return O, lse
+
+
+def attn_recovery(Q, K, ctx_len, idx, count, scale, Hkv):
+    """Share of the dense attention probability on I_b plus the new tokens 0..t.
+    Q: uint16 [B][n_verify][Hq][d]; K: uint16 [B][n_cap][Hkv][d]; idx int32 [B][k_max].
+    Returns float64 [B][Hq][n_verify]."""
+    Q, K, ctx_len, idx, count = _u16(Q), _u16(K), _i32(ctx_len), _i32(idx), _i32(count)
+    B, nv, Hq, d = Q.shape
+    n_cap = K.shape[1]
+    assert K.shape == (B, n_cap, Hkv, d)
+    rec = np.empty((B, Hq, nv), dtype=np.float64)
+    rc = lib().oracle_attn_recovery(B, Hq, Hkv, d, nv, _p(Q), _p(K), n_cap, _p(ctx_len), _p(idx),
+                                    _p(count), idx.shape[1], float(scale), _p(rec))
+    if rc:
+        raise ValueError(f"oracle_attn_recovery rc={rc}")
+    return rec
+
+
+def kv_write_block(Knew, Vnew, ctx_len, K, V):
+    """Returns copies of K, V ([B][n_cap][Hkv][d] uint16) with the block rows
+    Knew/Vnew [B][n_new][Hkv][d] stored at ctx_len[b] + j."""
+    Knew, Vnew, ctx_len = _u16(Knew), _u16(Vnew), _i32(ctx_len)
+    K, V = _u16(K).copy(), _u16(V).copy()
+    B, n_cap, Hkv, d = K.shape
+    n_new = Knew.shape[1]
+    assert Knew.shape == (B, n_new, Hkv, d) and Vnew.shape == Knew.shape and V.shape == K.shape
+    rc = lib().oracle_kv_write_block(B, Hkv, d, n_new, _p(Knew), _p(Vnew), _p(ctx_len), _p(K), _p(V), n_cap)
+    if rc:
+        raise ValueError(f"oracle_kv_write_block rc={rc}")
+    return K, V
+
+
+def kv_commit(ctx_len, n_accept, n_new):
+    """Returns the committed context lengths (int32 [B])."""
+    ctx = _i32(ctx_len).copy()
+    n_accept = _i32(n_accept)
+    rc = lib().oracle_kv_commit(ctx.shape[0], int(n_new), _p(n_accept), _p(ctx))
+    if rc:
+        raise ValueError(f"oracle_kv_commit rc={rc}")
+    return ctx
