@@ -192,6 +192,69 @@ def main():
                           "topk_select_us": round(timed(vs.select, reps), 2)}
         del vs
 
+    # Verification workflow step 5 and the draft phase around the step (not part of it):
+    # the verified block written into every layer's caches, the commit, and sparse
+    # attention with a single query (the sparse draft phase of the Vegas summary) on the
+    # same caches and selected set
+    from sparse_kv_attention_amd import dustin as D
+    g = torch.Generator(device=dev).manual_seed(1234)
+    kn = torch.randn((B, nv, T.hkv, T.d), generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn((B, nv, T.hkv, T.d), generator=g, device=dev).to(torch.bfloat16)
+    # the block rows are rewritten with themselves, so the caches stay as generated
+    ctxl = inp.ctx_len.cpu().tolist()
+    for b in range(B):
+        kn[b] = inp.k_cache[attn_layers[0]][b, ctxl[b]:ctxl[b] + nv]
+        vn[b] = inp.v_cache[attn_layers[0]][b, ctxl[b]:ctxl[b] + nv]
+    # these calls take a few µs of GPU time, less than their host-side launch cost, so they
+    # are timed as replays of a captured HIP graph of 80 back-to-back calls
+    def graph_timed(fn, n_calls=80, replays=10):
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(n_calls):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        return timed(graph.replay, replays) / n_calls
+
+    us_write = graph_timed(lambda: step.write_block(attn_layers[0], kn, vn))
+    n_acc = torch.full((B,), w.gamma, dtype=torch.int32, device=dev)
+    ctx_scratch = inp.ctx_len.clone()
+    us_commit = graph_timed(lambda: step.commit(n_acc, ctx_len=ctx_scratch))
+    q1 = {l: inp.q_verify[l][:, :1].contiguous() for l in attn_layers}
+    o1 = torch.empty((B, 1, T.hq, T.d), dtype=torch.bfloat16, device=dev)
+    l1 = torch.empty((B, T.hq, 1), dtype=torch.float32, device=dev)
+    ws1 = D.workspace(D.dustin_sparse_verify_attn_workspace_size(B, T.hq, T.hkv, T.d, 1, inp.k_max), dev)
+
+    def decode_all():
+        for l in attn_layers:
+            k, v = step.kv[l]
+            D.dustin_sparse_verify_attn(q1[l], k, v, T.hkv, inp.ctx_len, step.idx, step.count, step.scale,
+                                        o1, l1, ws1)
+    us_decode = timed(decode_all, reps) / len(attn_layers)
+    b_decode = attn_bytes(B, T.hq, T.hkv, T.d, 1, counts)
+    rec_layers = [l for l in (attn_layers[0], 60) if l in step.kv]
+    recovery = {}
+    for l in rec_layers:
+        r = step.recovery(l)
+        torch.cuda.synchronize()
+        recovery[f"layer_{l}"] = {"mean": round(float(r.mean()), 5), "min": round(float(r.min()), 5),
+                                  "max": round(float(r.max()), 5)}
+    # the whole step captured once as a HIP graph and replayed (same kernels, same order)
+    us_step_graph = graph_timed(step.step, n_calls=1, replays=args.steps)
+    us_attn_graph = graph_timed(lambda: [step.attn(l) for l in attn_layers], n_calls=1, replays=reps) / len(attn_layers)
+    step_extras = {
+        "step_us_graph_replay": round(us_step_graph, 1),
+        "attn_per_call_graph_replay_us": round(us_attn_graph, 2),
+        "kv_write_block_us": round(us_write, 2),
+        "kv_write_block_bytes": 2 * 2 * B * nv * T.hkv * T.d * 2,
+        "kv_commit_us": round(us_commit, 2),
+        "sparse_decode_nv1_per_call_us": round(us_decode, 2),
+        "sparse_decode_nv1_gbs": round(b_decode / (us_decode * 1e-6) / 1e9, 1),
+        "attn_recovery": recovery,
+    }
+
     # ---- bytes ----
     n_ctx = inp.n_max
     b_attn = attn_bytes(B, T.hq, T.hkv, T.d, nv, counts)
@@ -229,6 +292,7 @@ def main():
         "score_gbs": round(b_score / (us_score * 1e-6) / 1e9, 1),
         "dense_attn_per_layer_us": round(us_dense_layer, 2),
         "target_signal_variants": variants,
+        "around_the_step": step_extras,
         "dense_attn_gbs": round(b_dense / (us_dense_layer * 1e-6) / 1e9, 1),
         "attn_speedup_vs_dense": round(us_dense_layer / us_attn_call, 2),
         "wall_s_timed": round(wall, 3),

@@ -1,8 +1,8 @@
 /*
  * dustin.h — C ABI of the MI355X (gfx950) sparse-verification library.
  *
- * The three calls follow the middle steps of the verification workflow in the English
- * Dustin summary ("Methodology" 3, steps 2-4):
+ * The calls follow the steps of the verification workflow in the English
+ * Dustin summary ("Methodology" 3, steps 2-5):
  *   dustin_srh_score          step 2: the importance map, computed from the semantic
  *                             retrieval heads only ("Methodology" 1 and 2)
  *   dustin_select             step 3: the fixed-size verification set I_verify
@@ -11,6 +11,10 @@
  *                             selected tokens only
  *   dense_verify_attn         the full-cache verification it replaces ("Problem
  *                             Statement": the target loads the full KV cache)
+ *   dustin_kv_write_block,    step 5: the verified block in the cache; accepted tokens
+ *   dustin_kv_commit          are kept, rejected ones discarded
+ *   dustin_attn_recovery      the share of full-cache attention mass the kept set
+ *                             carries ("Methodology" 2: attention recovery rate)
  *
  * Conventions for every call
  *   - Pointers are DEVICE pointers unless marked (host).  bf16 data are raw 16-bit
@@ -177,6 +181,45 @@ dustin_status dense_verify_attn(int B, int Hq, int Hkv, int head_dim, int n_veri
                                 const dustin_kv_view *v /* host */, const int32_t *ctx_len,
                                 int n_max, float scale, void *out, float *lse,
                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Step 5 — the verified block in the cache (English Dustin summary, Verification
+ * Workflow step 5: accepted tokens are appended to the cache, rejected ones discarded).
+ *
+ * dustin_kv_write_block stores the block being verified behind the committed context,
+ * where dustin_sparse_verify_attn and dense_verify_attn read the new tokens:
+ *   K[b][ctx_len[b] + j][g] = k_new[b][j][g] and V likewise, for j < n_new, g < Hkv
+ *   k_new, v_new : bf16 [B][n_new][Hkv][head_dim], contiguous, 16-byte aligned
+ *   k, v         : (host) views of the two caches.  The call WRITES through them (their
+ *                  base pointers are const in the struct because every other call only
+ *                  reads); the K and V caches must not overlap.
+ *   ctx_len[b] is clamped to [0, min(capacity of k, capacity of v) - n_new] and is not
+ *   changed.  head_dim in {64, 128}; 1 <= n_new <= 16.
+ *
+ * dustin_kv_commit runs once verification has decided: the block's first row (the token
+ * produced by the previous step) and its first n_accept[b] draft rows are kept, the rows
+ * behind the new length are discarded (the next block overwrites them):
+ *   ctx_len[b] <- clamp(ctx_len[b], 0, 2^30) + 1 + clamp(n_accept[b], 0, n_new - 1)
+ *   n_accept, ctx_len : int32 [B] (device; ctx_len in/out); 1 <= n_new <= 16
+ * ------------------------------------------------------------------------------- */
+dustin_status dustin_kv_write_block(int B, int Hkv, int head_dim, int n_new, const void *k_new,
+                                    const void *v_new, const int32_t *ctx_len,
+                                    const dustin_kv_view *k /* host */,
+                                    const dustin_kv_view *v /* host */, void *stream);
+dustin_status dustin_kv_commit(int B, int n_new, const int32_t *n_accept, int32_t *ctx_len,
+                               void *stream);
+
+/* ---------------------------------------------------------------------------------
+ * Attention recovery.  The English Dustin summary ("Methodology" 2) picks its SRHs to
+ * maximise an attention recovery rate that it does not define; read here as the share of
+ * the full-cache attention probability that falls on the kept set.  Given the lse of a
+ * dustin_sparse_verify_attn call and of a dense_verify_attn call on the same queries and
+ * caches (both natural logs of their softmax normalisers), that share is
+ *   rec[i] = exp(lse_sparse[i] - lse_dense[i]),   0 <= i < n
+ * for every (b, h, t) of the [B][Hq][n_verify] layout.  All arrays fp32, device.
+ * ------------------------------------------------------------------------------- */
+dustin_status dustin_attn_recovery(int n, const float *lse_sparse, const float *lse_dense,
+                                   float *rec, void *stream);
 
 #ifdef __cplusplus
 }

@@ -5,6 +5,7 @@
 #include <algorithm>
 
 #include "dustin.h"
+#include "kv.hpp"
 #include "launch.hpp"
 
 using namespace dustin;
@@ -404,6 +405,61 @@ dustin_status dense_verify_attn(int B, int Hq, int Hkv, int head_dim, int n_veri
 {
     return run_attn(B, Hq, Hkv, head_dim, n_verify, q, k, v, ctx_len, nullptr, nullptr, 0, n_max,
                     scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+dustin_status dustin_kv_write_block(int B, int Hkv, int head_dim, int n_new, const void *k_new,
+                                    const void *v_new, const int32_t *ctx_len, const dustin_kv_view *k,
+                                    const dustin_kv_view *v, void *stream)
+{
+    if (B < 0 || Hkv <= 0 || n_new <= 0)
+        return DUSTIN_ERR_INVALID_ARG;
+    if ((head_dim != 64 && head_dim != 128) || n_new > kMaxNewRows)
+        return DUSTIN_ERR_UNSUPPORTED;
+    if (B == 0)
+        return DUSTIN_OK;
+    if (!k_new || !v_new || !ctx_len || !aligned16(k_new) || !aligned16(v_new))
+        return DUSTIN_ERR_INVALID_ARG;
+    if (!view_ok(k, Hkv, n_new) || !view_ok(v, Hkv, n_new))
+        return DUSTIN_ERR_INVALID_ARG;
+    KvWriteArgs a;
+    a.B = B;
+    a.Hkv = Hkv;
+    a.n_new = n_new;
+    a.k_new = static_cast<const uint16_t *>(k_new);
+    a.v_new = static_cast<const uint16_t *>(v_new);
+    a.k = make_view(*k);
+    a.v = make_view(*v);
+    a.ctx_len = ctx_len;
+    a.ctx_clamp = std::min(view_cap(k), view_cap(v)) - n_new;
+    const hipError_t e = launch_kv_write_block(a, head_dim, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
+}
+
+dustin_status dustin_kv_commit(int B, int n_new, const int32_t *n_accept, int32_t *ctx_len, void *stream)
+{
+    if (B < 0 || n_new <= 0)
+        return DUSTIN_ERR_INVALID_ARG;
+    if (n_new > kMaxNewRows)
+        return DUSTIN_ERR_UNSUPPORTED;
+    if (B == 0)
+        return DUSTIN_OK;
+    if (!n_accept || !ctx_len)
+        return DUSTIN_ERR_INVALID_ARG;
+    const hipError_t e = launch_kv_commit(B, n_new, n_accept, ctx_len, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
+}
+
+dustin_status dustin_attn_recovery(int n, const float *lse_sparse, const float *lse_dense, float *rec,
+                                   void *stream)
+{
+    if (n < 0)
+        return DUSTIN_ERR_INVALID_ARG;
+    if (n == 0)
+        return DUSTIN_OK;
+    if (!lse_sparse || !lse_dense || !rec)
+        return DUSTIN_ERR_INVALID_ARG;
+    const hipError_t e = launch_attn_recovery(n, lse_sparse, lse_dense, rec, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
 }
 
 }  // extern "C"

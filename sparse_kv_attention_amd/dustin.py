@@ -72,11 +72,16 @@ _sparse = _decl("dustin_sparse_verify_attn", [_I, _I, _I, _I, _I, _P, ctypes.POI
 _dense_ws = _decl("dense_verify_attn_workspace_size", [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)])
 _dense = _decl("dense_verify_attn", [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView),
                                      ctypes.POINTER(KvView), _P, _I, _F, _P, _P, _P, _SZ, _P])
+_kv_write = _decl("dustin_kv_write_block", [_I, _I, _I, _I, _P, _P, _P, ctypes.POINTER(KvView),
+                                             ctypes.POINTER(KvView), _P])
+_kv_commit = _decl("dustin_kv_commit", [_I, _I, _P, _P, _P])
+_recovery = _decl("dustin_attn_recovery", [_I, _P, _P, _P, _P])
 
 EXPORTED = ("dustin_status_string", "dustin_srh_score_workspace_size", "dustin_srh_score",
             "dustin_select_workspace_size", "dustin_select",
             "dustin_sparse_verify_attn_workspace_size", "dustin_sparse_verify_attn",
-            "dense_verify_attn_workspace_size", "dense_verify_attn")
+            "dense_verify_attn_workspace_size", "dense_verify_attn",
+            "dustin_kv_write_block", "dustin_kv_commit", "dustin_attn_recovery")
 
 
 class DustinError(RuntimeError):
@@ -232,6 +237,42 @@ def dense_verify_attn(q, k: KvView, v: KvView, Hkv: int, ctx_len, n_max: int, sc
     _check(_dense(B, Hq, Hkv, d, nv, _ptr(q), ctypes.byref(k), ctypes.byref(v), _ptr(ctx_len), int(n_max),
                   float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)),
            "dense_verify_attn")
+
+
+# ------------------------------------------------------------------- KV block, recovery
+
+def dustin_kv_write_block(k_new, v_new, ctx_len, k: KvView, v: KvView, stream=None):
+    """k_new, v_new: contiguous bf16 [B][n_new][Hkv][d]; rows go to ctx_len[b] + j of the
+    caches behind the views k and v (written)."""
+    _dev_i32(ctx_len, "ctx_len")
+    for t in (k_new, v_new):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4 or not t.is_cuda:
+            raise ValueError("k_new and v_new must be contiguous bf16 device tensors [B][n_new][Hkv][d]")
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must have the same shape")
+    B, n_new, Hkv, d = k_new.shape
+    _check(_kv_write(B, Hkv, d, n_new, _ptr(k_new), _ptr(v_new), _ptr(ctx_len), ctypes.byref(k),
+                     ctypes.byref(v), _stream(stream)), "dustin_kv_write_block")
+
+
+def dustin_kv_commit(n_accept, ctx_len, n_new: int, stream=None):
+    """ctx_len[b] += 1 + n_accept[b] (clamped as the header states), in place."""
+    _dev_i32(n_accept, "n_accept"); _dev_i32(ctx_len, "ctx_len")
+    if n_accept.shape != ctx_len.shape or n_accept.dim() != 1:
+        raise ValueError("n_accept and ctx_len must both be [B]")
+    _check(_kv_commit(ctx_len.shape[0], int(n_new), _ptr(n_accept), _ptr(ctx_len), _stream(stream)),
+           "dustin_kv_commit")
+
+
+def dustin_attn_recovery(lse_sparse, lse_dense, rec, stream=None):
+    """rec = exp(lse_sparse - lse_dense), elementwise over same-shaped contiguous fp32 tensors."""
+    for t in (lse_sparse, lse_dense, rec):
+        if t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("lse_sparse, lse_dense and rec must be contiguous fp32 device tensors")
+    if lse_sparse.shape != lse_dense.shape or rec.shape != lse_sparse.shape:
+        raise ValueError("lse_sparse, lse_dense and rec must have the same shape")
+    _check(_recovery(rec.numel(), _ptr(lse_sparse), _ptr(lse_dense), _ptr(rec), _stream(stream)),
+           "dustin_attn_recovery")
 
 
 def raw_library():

@@ -3,8 +3,9 @@
 Holds the views, workspaces and output buffers of a workload and issues the library
 calls in the order of the verification workflow (English Dustin summary, "Methodology"
 3, steps 2-4): score the draft SRHs, score the target SRHs, select I_verify, then
-verify attention layer by layer.  Argument marshalling only; all arithmetic runs in
-the HIP kernels.
+verify attention layer by layer; step 5 (the verified block in the cache) and the
+attention-recovery measurement are separate methods.  Argument marshalling only; all
+arithmetic runs in the HIP kernels.
 """
 from __future__ import annotations
 
@@ -95,6 +96,26 @@ class SparseVerifyStep:
         D.dense_verify_attn(self.inp.q_verify[layer], k, v, self.T.hkv, self.inp.ctx_len, self.n_max,
                             self.scale, self.out if out is None else out, self.lse if lse is None else lse,
                             self.ws_attn, stream)
+
+    def recovery(self, layer: int, rec=None, stream=None):
+        """Share of the dense attention mass on the kept set, per (b, h, t) [B][Hq][n_verify]:
+        one sparse and one dense call on the layer, then the library's recovery kernel."""
+        lse_s = torch.empty_like(self.lse)
+        lse_d = torch.empty_like(self.lse)
+        rec = torch.empty_like(self.lse) if rec is None else rec
+        self.attn(layer, out=torch.empty_like(self.out), lse=lse_s, stream=stream)
+        self.dense(layer, out=torch.empty_like(self.out), lse=lse_d, stream=stream)
+        D.dustin_attn_recovery(lse_s, lse_d, rec, stream)
+        return rec
+
+    def write_block(self, layer: int, k_new, v_new, ctx_len=None, stream=None):
+        """Store a block [B][n_new][Hkv][d] behind the committed context of a layer's caches."""
+        k, v = self.kv[layer]
+        D.dustin_kv_write_block(k_new, v_new, self.inp.ctx_len if ctx_len is None else ctx_len, k, v, stream)
+
+    def commit(self, n_accept, ctx_len=None, stream=None):
+        """Advance the context lengths (in place) over the kept rows of the verified block."""
+        D.dustin_kv_commit(n_accept, self.inp.ctx_len if ctx_len is None else ctx_len, self.inp.w.n_verify, stream)
 
     def step(self, stream=None):
         """One whole sparse-verification step: both signals, selection, every layer."""

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names
     assert set(names) == set(D.EXPORTED)
     out = subprocess.run(["nm", "-D", "--defined-only", D.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -152,3 +152,35 @@ def test_select_rejects():
     assert f(st=None) == D.ERR_INVALID_ARG
     assert f(idx=None) == D.ERR_INVALID_ARG
     assert f(k_max=-1) == D.ERR_INVALID_ARG
+
+
+def test_kv_write_block_rejects():
+    k = view()
+    small = view(n_tokens=4)
+
+    def f(B=2, Hkv=8, d=128, n_new=5, kn=FAKE, vn=FAKE, ctx=FAKE, kv=k, vv=k):
+        return D._kv_write(B, Hkv, d, n_new, kn, vn, ctx, ctypes.byref(kv), ctypes.byref(vv), None)
+
+    assert f(d=96) == D.ERR_UNSUPPORTED
+    assert f(n_new=17) == D.ERR_UNSUPPORTED
+    assert f(n_new=0) == D.ERR_INVALID_ARG
+    assert f(Hkv=0) == D.ERR_INVALID_ARG
+    assert f(B=-1) == D.ERR_INVALID_ARG
+    assert f(kn=None) == D.ERR_INVALID_ARG
+    assert f(vn=FAKE + 8) == D.ERR_INVALID_ARG
+    assert f(ctx=None) == D.ERR_INVALID_ARG
+    assert f(kv=small) == D.ERR_INVALID_ARG          # the block does not fit the view
+    assert f(vv=view(n_heads=4)) == D.ERR_INVALID_ARG
+    assert f(B=0, kn=None, vn=None, ctx=None) == D.OK
+
+
+def test_kv_commit_and_recovery_reject():
+    assert D._kv_commit(2, 0, FAKE, FAKE, None) == D.ERR_INVALID_ARG
+    assert D._kv_commit(2, 17, FAKE, FAKE, None) == D.ERR_UNSUPPORTED
+    assert D._kv_commit(2, 5, None, FAKE, None) == D.ERR_INVALID_ARG
+    assert D._kv_commit(2, 5, FAKE, None, None) == D.ERR_INVALID_ARG
+    assert D._kv_commit(0, 5, None, None, None) == D.OK
+    assert D._recovery(-1, FAKE, FAKE, FAKE, None) == D.ERR_INVALID_ARG
+    assert D._recovery(10, None, FAKE, FAKE, None) == D.ERR_INVALID_ARG
+    assert D._recovery(10, FAKE, FAKE, None, None) == D.ERR_INVALID_ARG
+    assert D._recovery(0, None, None, None, None) == D.OK

@@ -1,0 +1,190 @@
+"""GPU parity of the verified block in the cache (English Dustin summary, Verification
+Workflow step 5) and of the attention-recovery measurement, through the C ABI.
+
+Bars: the block write and the commit are byte/integer work, so bit-exact against the
+oracle; recovery is exp(LSE_sparse - LSE_dense) of two attention calls whose LSEs are
+each within 1e-3 of the oracle's, so it is checked within exp(2e-3) - 1 relative of the
+oracle's direct sum of dense probabilities over the kept set.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from _harness import LSE_ATOL, rows, say, u16
+from oracle import oracle as O
+from sparse_kv_attention_amd import dustin as D
+from sparse_kv_attention_amd import workloads as W
+from sparse_kv_attention_amd.pipeline import SparseVerifyStep
+from test_parity_gpu import small
+
+pytestmark = pytest.mark.gpu
+
+REC_RTOL = math.exp(2 * LSE_ATOL) - 1.0
+
+
+def logical(inp, cache, n_rows):
+    return np.stack([u16(rows(inp, cache, b, n_rows)) for b in range(inp.w.batch)])
+
+
+def allocated_rows(inp):
+    """Rows of each sequence that its own pages hold (all rows when contiguous)."""
+    if not inp.paged:
+        return [inp.n_cap] * inp.w.batch
+    ps = inp.w.page_size
+    ctx = inp.ctx_len.cpu().numpy()
+    return [(int(ctx[b]) + inp.w.n_verify + ps - 1) // ps * ps for b in range(inp.w.batch)]
+
+
+def check_write(inp, n_new, ctx_override=None, seed=0):
+    w = inp.w
+    T = w.target
+    B = w.batch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    kn = torch.randn((B, n_new, T.hkv, T.d), generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((B, n_new, T.hkv, T.d), generator=g, device="cuda").to(torch.bfloat16)
+    ctx = inp.ctx_len if ctx_override is None else ctx_override
+    kc, vc = inp.k_cache[0], inp.v_cache[0]
+    n_rows = max(allocated_rows(inp))
+    k_before, v_before = logical(inp, kc, n_rows), logical(inp, vc, n_rows)
+    phys_k, phys_v = kc.clone(), vc.clone()
+    step = SparseVerifyStep(inp, layers=[0])
+    say(f"[{w.name}] kv write block n_new={n_new} paged={inp.paged}")
+    step.write_block(0, kn, vn, ctx_len=ctx)
+    torch.cuda.synchronize()
+    # the oracle on the clamped lengths (the view's capacity bounds where a block may go)
+    cap = kc.shape[1] if not inp.paged else inp.page_table.shape[1] * w.page_size
+    ctx_c = np.clip(ctx.cpu().numpy(), 0, cap - n_new).astype(np.int32)
+    k_want, v_want = O.kv_write_block(u16(kn), u16(vn), ctx_c, k_before, v_before)
+    k_got, v_got = logical(inp, kc, n_rows), logical(inp, vc, n_rows)
+    for b, n_alloc in enumerate(allocated_rows(inp)):
+        assert np.array_equal(k_got[b, :n_alloc], k_want[b, :n_alloc]), f"K rows of sequence {b}"
+        assert np.array_equal(v_got[b, :n_alloc], v_want[b, :n_alloc]), f"V rows of sequence {b}"
+    # no physical row outside the block changed
+    changed = int((kc != phys_k).any(-1).sum() + (vc != phys_v).any(-1).sum())
+    assert changed <= 2 * B * n_new * T.hkv, changed
+    say(f"  bit-exact; {changed} physical head rows rewritten")
+
+
+def test_write_block_contiguous_head_dim_64():
+    inp = W.make_inputs(W.TINY, device="cuda")
+    check_write(inp, inp.w.n_verify)
+
+
+def test_write_block_contiguous_widest_block_at_capacity():
+    w = small("kv_edges", 4, 400, 8, 2, 128, 15, 64, 4, 8, 16, seed=21)
+    inp = W.make_inputs(w, device="cuda")
+    # lengths 0, the largest that fits, and out-of-range values the kernel clamps
+    ctx = torch.tensor([0, inp.n_cap - 16, -7, 1 << 30], dtype=torch.int32, device="cuda")
+    check_write(inp, 16, ctx_override=ctx, seed=1)
+    check_write(inp, 1, seed=2)
+
+
+def test_write_block_paged():
+    w = W.shrink(W.RAGGED_PAGED, batch=6, n_ctx=3000, ragged_lo=700, target=W.ModelShape(1, 64, 8, 128),
+                 srh_target=((0, 0),))
+    inp = W.make_inputs(w, device="cuda")
+    check_write(inp, w.n_verify, seed=3)
+
+
+def test_write_block_qwen72b_layer_full_size():
+    inp = W.make_inputs(W.shrink(W.QWEN72B, target=W.ModelShape(1, 64, 8, 128), srh_target=((0, 0),),
+                                 needle_mode="none"), device="cuda")
+    check_write(inp, inp.w.n_verify, seed=4)
+    del inp
+    torch.cuda.empty_cache()
+
+
+def test_round_trip_write_then_attend():
+    # the new-token rows of the generated cache, moved out to a staging block, zeroed, and
+    # written back by the library: attention must be bitwise what it was
+    inp = W.make_inputs(W.shrink(W.QWEN7B, target=W.ModelShape(1, 28, 4, 128), srh_target=((0, 0),)),
+                        device="cuda")
+    step = SparseVerifyStep(inp, layers=[0])
+    step.score()
+    step.select()
+    step.attn(0)
+    o0, l0 = step.out.clone(), step.lse.clone()
+    ctx = inp.ctx_len.cpu().tolist()
+    nv = inp.w.n_verify
+    kc, vc = inp.k_cache[0], inp.v_cache[0]
+    kn = torch.stack([kc[b, ctx[b]:ctx[b] + nv] for b in range(inp.w.batch)]).contiguous()
+    vn = torch.stack([vc[b, ctx[b]:ctx[b] + nv] for b in range(inp.w.batch)]).contiguous()
+    for b in range(inp.w.batch):
+        kc[b, ctx[b]:ctx[b] + nv] = 0
+        vc[b, ctx[b]:ctx[b] + nv] = 0
+    step.write_block(0, kn, vn)
+    step.attn(0)
+    torch.cuda.synchronize()
+    assert torch.equal(step.out, o0) and torch.equal(step.lse, l0)
+
+
+def test_commit():
+    B, n_new = 37, 5
+    rng = np.random.default_rng(7)
+    ctx = rng.integers(0, 70000, B).astype(np.int32)
+    acc = rng.integers(0, n_new, B).astype(np.int32)
+    c_dev = torch.from_numpy(ctx).cuda()
+    a_dev = torch.from_numpy(acc).cuda()
+    D.dustin_kv_commit(a_dev, c_dev, n_new)
+    torch.cuda.synchronize()
+    assert np.array_equal(c_dev.cpu().numpy(), O.kv_commit(ctx, acc, n_new))
+    # out-of-range acceptance counts act as their clamped values
+    bad = np.array([-3, 99, 4, 0], np.int32)
+    c_dev = torch.tensor([10, 10, 10, 10], dtype=torch.int32, device="cuda")
+    D.dustin_kv_commit(torch.from_numpy(bad).cuda(), c_dev, n_new)
+    torch.cuda.synchronize()
+    assert np.array_equal(c_dev.cpu().numpy(), O.kv_commit([10] * 4, np.clip(bad, 0, n_new - 1), n_new))
+
+
+def check_recovery(inp, layer, bsel, heads=None):
+    w = inp.w
+    T = w.target
+    step = SparseVerifyStep(inp, layers=[layer])
+    step.score()
+    step.select()
+    rec = step.recovery(layer)
+    torch.cuda.synchronize()
+    idx, cnt = step.idx.cpu().numpy(), step.count.cpu().numpy()
+    ctx = inp.ctx_len.cpu().numpy()
+    n_rows = int(ctx[bsel].max()) + w.n_verify
+    got = rec.cpu().numpy()
+    heads = list(range(T.hkv)) if heads is None else heads
+    worst = 0.0
+    for g in heads:                      # one KV head's query group at a time
+        hs = slice(g * T.group, (g + 1) * T.group)
+        K = np.stack([u16(rows(inp, inp.k_cache[layer], b, n_rows)[:, g:g + 1]) for b in bsel])
+        Q = u16(inp.q_verify[layer][bsel][:, :, hs])
+        ref = O.attn_recovery(Q, K, ctx[bsel], idx[bsel][:, :inp.k_max], cnt[bsel], 1.0 / math.sqrt(T.d), 1)
+        err = np.abs(got[bsel][:, hs] - ref) / ref
+        worst = max(worst, float(err.max()))
+    say(f"  [{w.name}] recovery: mean {got[bsel].mean():.4f}, max rel err {worst:.3g} (bar {REC_RTOL:.3g})")
+    assert worst <= REC_RTOL
+    return got
+
+
+def test_recovery_qwen7b():
+    inp = W.make_inputs(W.QWEN7B, device="cuda", target_layers=[0])
+    check_recovery(inp, 0, np.arange(4))
+
+
+def test_recovery_full_budget_is_one():
+    w = small("rec_full", 2, 300, 8, 2, 128, 4, 300, 4, 16, 40, seed=12)
+    inp = W.make_inputs(w, device="cuda")
+    got = check_recovery(inp, 0, np.arange(2))
+    assert np.all(got == 1.0)
+
+
+def test_recovery_ragged_paged():
+    w = W.shrink(W.RAGGED_PAGED, batch=4, n_ctx=9000, ragged_lo=1000, target=W.ModelShape(1, 64, 8, 128),
+                 srh_target=((0, 0), (0, 8)))
+    inp = W.make_inputs(w, device="cuda")
+    check_recovery(inp, 0, np.arange(4), heads=[0, 7])
+
+
+def test_recovery_qwen72b_sampled():
+    inp = W.make_inputs(W.QWEN72B, device="cuda", target_layers=[60])
+    check_recovery(inp, 60, np.array([0]), heads=[0, 5])
+    del inp
+    torch.cuda.empty_cache()
