@@ -18,6 +18,8 @@ size) from the committed counter summary, and null when the kernel source has ch
 since those counters were taken.
 
 `--counters` runs only a calibration copy and the attention calls, for counter passes.
+`--estimator-sweep` times the naive all-heads estimator, dense attention and the SRH
+scoring at contexts 1k..64k instead of the step (one JSON line of its own).
 """
 from __future__ import annotations
 
@@ -88,6 +90,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
     ap.add_argument("--dense-layers", type=int, default=8)
     ap.add_argument("--counters", action="store_true", help="calibration copy + attention calls only")
+    ap.add_argument("--estimator-sweep", action="store_true",
+                    help="naive all-heads estimator vs dense attention vs SRH scoring, context 1k..64k")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -101,6 +105,9 @@ def main():
     from sparse_kv_attention_amd.pipeline import SparseVerifyStep
 
     dev = torch.device("cuda:0")
+    if args.estimator_sweep:
+        estimator_sweep(dev, args)
+        return
     w = W.QWEN72B
     if args.layers != w.target.layers:
         w = W.shrink(w, target=W.ModelShape(args.layers, w.target.hq, w.target.hkv, w.target.d),
@@ -306,6 +313,66 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, step, args.cpu_seconds, b_attn, b_score, b_select, attn_layers)
     print(json.dumps(line), flush=True)
+
+
+def estimator_sweep(dev, args):
+    """The naive estimator against full-cache attention as the context grows (English Dustin
+    summary, "Problem Statement": materialising attention scores over all heads and layers
+    costs more than full-cache attention beyond 4k tokens; "Experimental Results": the SRH
+    estimation is under 1% of full-cache latency).  Qwen2.5-72B-shaped target with the
+    0.5B-shaped draft, batch 8, gamma 4, contexts 1k..64k.  Per context length, one target
+    layer and one draft layer are timed and multiplied by the layer counts (80 and 24; every
+    layer has the same shape and cost); the SRH scoring is the real one (both signals, all
+    8 SRH streams).  Prints one JSON line."""
+    import torch
+
+    from sparse_kv_attention_amd import workloads as W
+    from sparse_kv_attention_amd.pipeline import AllHeadsEstimator, SparseVerifyStep
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    points = []
+    for n in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
+        w = W.shrink(W.QWEN72B, n_ctx=n, budget=min(2048, n // 4), n_window=min(256, n // 32),
+                     m=min(768, 3 * n // 32), needle_mode="none")
+        inp = W.make_inputs(w, device=dev, target_layers=[0])
+        T, Dm = w.target, w.draft
+        step = SparseVerifyStep(inp, layers=[0])
+        q_t = inp.q_verify[0].permute(0, 2, 1, 3).contiguous()            # [B][Hq][gamma+1][d]
+        g = torch.Generator(device=dev).manual_seed(n)
+        q_d = torch.randn((w.batch, Dm.hq, w.gamma, Dm.d), generator=g, device=dev).to(torch.bfloat16)
+        est_t = AllHeadsEstimator(inp.k_cache[0], None, q_t, T.hkv, inp.ctx_len, 1.0 / math.sqrt(T.d))
+        est_d = AllHeadsEstimator(inp.draft_k[2], None, q_d, Dm.hkv, inp.ctx_len, 1.0 / math.sqrt(Dm.d))
+        reps = max(3, min(20, (1 << 17) // n))
+        us_t = timed(est_t.score, reps)
+        us_d = timed(est_d.score, reps)
+        us_dense = timed(lambda: step.dense(0), reps)
+        us_srh = timed(step.score, reps)
+        naive = T.layers * us_t + Dm.layers * us_d
+        dense = T.layers * us_dense
+        points.append({"ctx": n, "naive_target_layer_us": round(us_t, 2), "naive_draft_layer_us": round(us_d, 2),
+                       "dense_layer_us": round(us_dense, 2), "naive_all_layers_us": round(naive, 1),
+                       "dense_all_layers_us": round(dense, 1), "srh_scoring_us": round(us_srh, 2),
+                       "naive_over_dense": round(naive / dense, 3), "srh_over_dense": round(us_srh / dense, 5),
+                       "naive_calls_per_layer": {"target": len(est_t.calls), "draft": len(est_d.calls)}})
+        print(f"# ctx {n}: {points[-1]}", file=sys.stderr, flush=True)
+        del step, est_t, est_d, inp
+        torch.cuda.empty_cache()
+    print(json.dumps({"estimator_sweep": points, "batch": 8, "gamma": 4,
+                      "target": "80 layers x 64 q-heads / 8 KV heads, d 128",
+                      "draft": "24 layers x 14 q-heads / 2 KV heads, d 64",
+                      "layer_extrapolation": "one layer of each model timed, times its layer count"}), flush=True)
 
 
 def cpu_baseline(inp, step, budget_s, b_attn, b_score, b_select, layers):

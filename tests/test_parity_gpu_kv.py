@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from _harness import LSE_ATOL, rows, say, u16
+from _harness import LSE_ATOL, check_scores, rows, say, u16
 from oracle import oracle as O
 from sparse_kv_attention_amd import dustin as D
 from sparse_kv_attention_amd import workloads as W
@@ -188,3 +188,31 @@ def test_recovery_qwen72b_sampled():
     check_recovery(inp, 60, np.array([0]), heads=[0, 5])
     del inp
     torch.cuda.empty_cache()
+
+
+def test_all_heads_estimator_widest_groups():
+    """The naive estimator's calls: every query head of a 72B-shaped layer (groups of 3, 3
+    and 2 heads x 5 queries = 15, 15, 10 pairs; calls of 16 and 8 groups) and of a draft
+    layer (4 and 3 heads x 4 queries = 16, 12 pairs), each call against the oracle."""
+    from sparse_kv_attention_amd.pipeline import AllHeadsEstimator
+    w = W.shrink(W.QWEN72B, batch=2, n_ctx=1500, target=W.ModelShape(1, 64, 8, 128), srh_target=((0, 0),),
+                 needle_mode="none")
+    inp = W.make_inputs(w, device="cuda")
+    ctx = inp.ctx_len.cpu().numpy()
+    cases = (("target", inp.k_cache[0], inp.q_verify[0].permute(0, 2, 1, 3).contiguous(), w.target),
+             ("draft", inp.draft_k[2], torch.randn((2, w.draft.hq, w.gamma, w.draft.d), device="cuda",
+                                                    generator=torch.Generator(device="cuda").manual_seed(5)
+                                                    ).to(torch.bfloat16), w.draft))
+    for name, kc, q, shape in cases:
+        est = AllHeadsEstimator(kc, None, q, shape.hkv, inp.ctx_len, 1.0 / math.sqrt(shape.d))
+        est.score()
+        torch.cuda.synchronize()
+        say(f"[{name}] {len(est.calls)} calls, pairs per group {[nh * q.shape[2] for _, _, nh in est.calls[0][0]]}")
+        for (groups, cq), got in zip(est.calls, est.scores):
+            acc = np.zeros((2, est.n_max))
+            h = 0
+            for _, g, nh in groups:
+                K = u16(kc[:, :est.n_max, g])
+                O.score_stream(K, u16(cq[:, h:h + nh]), ctx, est.n_max, 1.0 / math.sqrt(shape.d), O.PROB_SUM, acc)
+                h += nh
+            check_scores(got.cpu().numpy(), acc, f"{name} all-heads call")
