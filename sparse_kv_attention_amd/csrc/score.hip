@@ -4,12 +4,14 @@
 // Vegas summary 2A/2B for the logit-sum mode over the first and bonus queries).
 //
 // Softmax mode (PROB_SUM), two kernels:
-//   srh_prob_logits  one workgroup per (run of 256-token tiles, group, sequence); the grid
-//                    is sized to one resident round.  A tile's key rows are read with
-//                    coalesced non-temporal 16-byte loads into LDS, the next tile is
-//                    prefetched into registers.  The four lanes of a quad share four
-//                    tokens and split the head dim, so each fp64 query value read from LDS
-//                    feeds several tokens; the quad's partial dot products are combined by
+//   srh_prob_logits  one workgroup per (share of a stream's tiles, group, sequence); the
+//                    grid is one resident round of CU-filling workgroups.  Each wave
+//                    claims 64-token tiles from the workgroup's counter, reads a tile's
+//                    key rows with coalesced non-temporal 16-byte loads into its own LDS
+//                    area, and keeps the next tile in flight in registers; no workgroup
+//                    barrier is taken per tile.  The lanes of a token group share tokens
+//                    and split the head dim, so each fp64 query value read from LDS
+//                    feeds several tokens; the group's partial dot products are combined by
 //                    a DPP reduce-scatter, after which lane t holds token t of the tile.
 //                    Products of bf16 values are exact in fp64, so the only rounding is
 //                    fp64 accumulation.  Logits are stored as fp32 offsets from the maximum
@@ -140,11 +142,25 @@ __device__ __forceinline__ double quad_xor(double v)
     return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
+// Waves per workgroup of the softmax-mode logit kernel.  One workgroup fills a CU, so all
+// of a CU's waves draw tiles from one counter and none is left running alone at the end.
+// Groups of more than 8 pairs need a lane's whole register file (one wave per SIMD), the
+// others run two waves per SIMD (three, possible for the 140-register matrix-core variant,
+// measured slower: the third wave's tiles only add to the requests queued at the start).
+template <int D, int PC>
+constexpr int prob_waves()
+{
+    return PC > 8 ? 4 : 8;
+}
+
 // FLAT: every group's view is unpaged with a row stride below 4 GiB, so a row address is a
 // per-workgroup base plus token x stride (one 32x32->64 multiply-add per load).
 template <int D, int PC, bool FLAT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8 ? 1 : 2))) void srh_prob_logits_kernel(ScoreArgs a)
+__global__ __launch_bounds__((64 * prob_waves<D, PC>()))
+__attribute__((amdgpu_waves_per_eu((prob_waves<D, PC>() / 4)))) void srh_prob_logits_kernel(ScoreArgs a)
 {
+    constexpr int NW = prob_waves<D, PC>();
+    constexpr int NT = 64 * NW;
     // groups of 4 pairs: the dot products run on the fp64 matrix cores
     constexpr bool MF = PC == 4;
     // lanes per token group = tokens per lane: 4 where registers allow (each query value
@@ -157,11 +173,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
     constexpr int RB = D * 2;          // bytes per key row
     constexpr int RSTR = RB + 16;      // LDS row stride (conflict-free 16-byte row reads)
     constexpr int CPR = RB / 16;       // 16-byte chunks per row
-    constexpr int LPT = kProbTile * CPR / kThreads;   // 16-byte loads per thread per tile
-    __shared__ __align__(16) uint8_t sK[kProbTile * RSTR];
+    constexpr int LPT = kStatTile * CPR / 64;   // 16-byte loads per lane per 64-token tile
+    __shared__ __align__(16) uint8_t sK[NW][kStatTile * RSTR];   // one tile per wave
     __shared__ __align__(16) double sQ[PC][D];
-    __shared__ double sRunM[4][PC];   // per wave: running max and sum of exp2(l - max)
-    __shared__ double sRunS[4][PC];
+    __shared__ double sRunM[NW][PC];   // per wave: running max and sum of exp2(l - max)
+    __shared__ double sRunS[NW][PC];
+    __shared__ int sNext;              // tiles claimed so far by the workgroup's waves
 
     const ScoreGroup &G = a.grp[blockIdx.y];
     const int b = blockIdx.z;
@@ -169,16 +186,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
-    const int n_live = (N + kProbTile - 1) / kProbTile;     // tiles holding context tokens
+    // 64-token tiles holding context tokens; this workgroup takes an equal share of them
+    const int n_live = (N + kStatTile - 1) / kStatTile;
+    const int q_lo = (int)((int64_t)n_live * blockIdx.x / gridDim.x);
+    const int q_hi = (int)((int64_t)n_live * (blockIdx.x + 1) / gridDim.x);
 
-    // statistics tiles past the live tiles: empty partials
-    for (int st = n_live * (kProbTile / kStatTile) + blockIdx.x; st < a.n_tiles; st += gridDim.x)
-        for (int p = tid; p < G.n_pairs; p += kThreads) {
+    // statistics tiles past the live tiles: empty
+    for (int st = n_live + blockIdx.x; st < a.n_tiles; st += gridDim.x)
+        for (int p = tid; p < G.n_pairs; p += NT) {
             const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_tiles + st;
             a.tile_max[e] = -INFINITY;
         }
-    if ((int)blockIdx.x >= n_live) {
-        for (int p = tid; p < G.n_pairs; p += kThreads) {
+    if (q_lo >= q_hi) {
+        for (int p = tid; p < G.n_pairs; p += NT) {
             const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_parts + blockIdx.x;
             a.part_max[e] = -INFINITY;
             a.part_sum[e] = 0.0;
@@ -189,7 +209,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
     double runM = -INFINITY, runS = 0.0;
 
     // the group's queries (fp64) stay in LDS for every tile of this workgroup
-    for (int e = tid; e < PC * D; e += kThreads) {
+    for (int e = tid; e < PC * D; e += NT) {
         const int p = e / D;
         const int dd = e - p * D;
         double qv = 0.0;
@@ -201,18 +221,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
         }
         sQ[p][dd] = qv;
     }
+    if (tid == 0)
+        sNext = 0;
+    __syncthreads();                  // queries and the tile counter ready
+    uint8_t *myK = sK[w];
 
-    // tile rows: thread tid loads chunks tid + i*256 (row = chunk / CPR), all issued at once
-    // kDepth tiles in flight in registers per thread.  Loads are unconditional (positions
-    // past the context read row N-1, which is discarded), so the waits count exactly.
+    // A wave's tile is 64 tokens: lane l loads chunks l + 64 i (row = chunk / CPR) of the
+    // tile's rows, all issued at once, kDepth tiles in flight in registers per lane.  Loads
+    // are unconditional (positions past the context, and tiles past the workgroup's share,
+    // read row N-1, which is discarded), so the waits count exactly.
     const char *flat_base = reinterpret_cast<const char *>(G.k.base + (int64_t)b * G.k.sb + (int64_t)G.kv_head * G.k.sh) +
-                            (tid % CPR) * 16;
+                            (lane % CPR) * 16;
     const uint32_t flat_st = (uint32_t)(G.k.st * 2);
     auto issue = [&](u32x4 (&kr)[LPT], int tile) {
-        const int t0 = tile * kProbTile;
+        const int t0 = tile * kStatTile;
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
-            const int c = tid + i * kThreads;
+            const int c = lane + i * 64;
             const int r = c / CPR;
             const int t = min(t0 + r, N - 1);
             const u32x4 *src;
@@ -223,23 +248,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
             kr[i] = __builtin_nontemporal_load(src);
         }
     };
+    // Only the wave itself reads its LDS tile, and a wave's LDS accesses complete in
+    // order, so no workgroup barrier is needed; the fences keep the compiler from moving
+    // LDS accesses across the staging.
     auto stage = [&](const u32x4 (&kr)[LPT]) {
-        __syncthreads();                  // previous tile's rows consumed
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
-            const int c = tid + i * kThreads;
+            const int c = lane + i * 64;
             const int r = c / CPR;
-            *reinterpret_cast<u32x4 *>(&sK[r * RSTR + (c - r * CPR) * 16]) = kr[i];
+            *reinterpret_cast<u32x4 *>(&myK[r * RSTR + (c - r * CPR) * 16]) = kr[i];
         }
+        wait_lgkm0();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     };
     auto process = [&](int tile) {
-        __syncthreads();
-
         // Dot products: S lanes share the S tokens S*g .. S*g+S-1 and split the head dim,
         // lane s taking the 16-byte chunks S*j+s (so the 16 lanes of an LDS pass hit
         // distinct banks).  Each query value read from LDS feeds KT tokens.
-        const int g = tid / S;
-        const int s = tid % S;
+        const int g = lane / S;
+        const int s = lane % S;
         double acc[S][PC];
 #pragma unroll
         for (int i = 0; i < S; ++i)
@@ -254,7 +284,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
                 double kv[KT][8];
 #pragma unroll
                 for (int i = 0; i < KT; ++i) {
-                    const u32x4 kw = *reinterpret_cast<const u32x4 *>(&sK[(S * g + i0 + i) * RSTR + ch * 16]);
+                    const u32x4 kw = *reinterpret_cast<const u32x4 *>(&myK[(S * g + i0 + i) * RSTR + ch * 16]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         kv[i][2 * e] = (double)bf16_lo(kw[e]);
@@ -277,8 +307,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
             }
         }
         // reduce-scatter over the S lanes: lane s ends with the full sums of token S*g+s,
-        // i.e. lane tid holds token tid of the tile
-        const int tok = tile * kProbTile + tid;
+        // i.e. lane l holds token l of the tile
+        const int tok = tile * kStatTile + lane;
         const bool valid = tok < N;
         double l[PC];
 #pragma unroll
@@ -302,12 +332,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
             l[p] = mine + quad_xor<1>(give);
         }
 
-        // ---- per wave (its 64 tokens are one statistics tile): per-pair maximum, offsets
-        // from it, sum of exp2.  The maximum is taken over the fp32-rounded logits (rounding
-        // is monotonic, so it is the rounded true maximum); it is the tile's reference and
-        // the offsets are formed against it in fp64.  All pairs go through each reduction
-        // step together. ----
-        const int stile = tile * (kProbTile / kStatTile) + w;
+        // ---- the wave's 64 tokens are one statistics tile: per-pair maximum, offsets from
+        // it, sum of exp2.  The maximum is taken over the fp32-rounded logits (rounding is
+        // monotonic, so it is the rounded true maximum); it is the tile's reference and the
+        // offsets are formed against it in fp64.  All pairs go through each reduction step
+        // together. ----
+        const int stile = tile;
         double lp[PC];
         float mf[PC], off[PC], ex[PC];
 #pragma unroll
@@ -335,7 +365,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
             m_l = lane == p ? mf[p] : m_l;
             s_l = lane == p ? ex[p] : s_l;
         }
-        if (lane < G.n_pairs && lane < PC && stile < a.n_tiles)   // a wave past n_tiles holds no token
+        if (lane < G.n_pairs && lane < PC && stile < a.n_tiles)
             a.tile_max[(row0 + lane) * a.n_tiles + stile] = (double)m_l;
         if (m_l > -INFINITY) {
             const double m = (double)m_l;
@@ -358,12 +388,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
     // part; the gain is in the query reads (one per 16 tokens) and the reduce-scatter that
     // is no longer needed.  A fifth pair on the vector unit made 5-pair groups slower.
     auto process_mf = [&](auto tile) {   // generic: only instantiated where it is called
-        __syncthreads();
         constexpr int DK = D / 4;
         const int kq = lane >> 4;
         const int t16 = lane & 15;
         const double *qa_row = &sQ[lane & 3][kq * DK];
-        const uint8_t *k_row = &sK[(64 * w + t16) * RSTR + kq * DK * 2];
+        const uint8_t *k_row = &myK[t16 * RSTR + kq * DK * 2];
         double cm[4] = {0.0, 0.0, 0.0, 0.0};
         // 8 head-dim elements (one 16-byte LDS read per token) at a time
 #pragma unroll 1
@@ -385,8 +414,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
         }
         // statistics of the wave's 64 tokens (one statistics tile) per pair: the maximum of
         // the fp32-rounded logits as the tile's reference, offsets against it, sum of exp2
-        const int stile = tile * (kProbTile / kStatTile) + w;
-        const int tok0 = tile * kProbTile + 64 * w + t16;      // + 16 g
+        const int stile = tile;
+        const int tok0 = tile * kStatTile + t16;               // + 16 g
         const int pr = lane >> 4;                              // the lane's pair
         double lm[4];
         float red[1] = {-INFINITY};
@@ -412,7 +441,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
             for (int g = 0; g < 4; ++g)
                 if (tok0 + 16 * g < N)
                     a.logits[(row0 + pr) * a.n_pad + tok0 + 16 * g] = off[g];
-            if (t16 == 0 && stile < a.n_tiles)   // a wave past n_tiles holds no token
+            if (t16 == 0 && stile < a.n_tiles)
                 a.tile_max[(row0 + pr) * a.n_tiles + stile] = (double)mx;
         }
         if (mx > -INFINITY) {
@@ -423,45 +452,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
             runM = M1;
         }
     };
-    const int step = gridDim.x;
-    int tile = blockIdx.x;
+    // Tiles are claimed one at a time from the workgroup's counter, so a wave that gets
+    // less of the SIMDs than its neighbours simply takes fewer tiles.  A wave's claims
+    // increase, so the loop ends at the first claim past the share (single exit: the
+    // compiler's waits then keep the second tile in flight).
+    auto claim = [&]() {
+        int v = 0;
+        if (lane == 0)
+            v = atomicAdd(&sNext, 1);
+        return q_lo + __builtin_amdgcn_readfirstlane(v);
+    };
+    int qa = claim();
     u32x4 krA[LPT];
-    issue(krA, tile);
+    issue(krA, qa);
     if constexpr (kDepth == 2) {
+        int qb = claim();
         u32x4 krB[LPT];
         __builtin_amdgcn_sched_barrier(0);   // krA's loads first, as in the loop
-        issue(krB, tile + step);
-        // one exit: the second half of the last pair may lie past the live tiles (its
-        // staged rows are then discarded)
-        const int pairs_of_tiles = ((n_live - tile + step - 1) / step + 1) / 2;
-        for (int k = 0; k < pairs_of_tiles; ++k) {
+        issue(krB, qb);
+        while (qa < q_hi) {
             stage(krA);
-            issue(krA, tile + 2 * step);
+            const int qc = claim();
+            issue(krA, qc);
             if constexpr (MF)
-                process_mf(tile);
+                process_mf(qa);
             else
-                process(tile);
+                process(qa);
             stage(krB);
-            issue(krB, tile + 3 * step);
-            if (tile + step < n_live) {
+            const int qd = claim();
+            issue(krB, qd);
+            if (qb < q_hi) {
                 if constexpr (MF)
-                    process_mf(tile + step);
+                    process_mf(qb);
                 else
-                    process(tile + step);
+                    process(qb);
             }
-            tile += 2 * step;
+            qa = qc;
+            qb = qd;
         }
     } else {
-        for (;;) {
+        while (qa < q_hi) {
             stage(krA);
-            issue(krA, tile + step);
+            const int qc = claim();
+            issue(krA, qc);
             if constexpr (MF)
-                process_mf(tile);
+                process_mf(qa);
             else
-                process(tile);
-            tile += step;
-            if (tile >= n_live)
-                break;
+                process(qa);
+            qa = qc;
         }
     }
     {
@@ -478,11 +516,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PC > 8
         const int p = tid;
         double M = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < NW; ++v)
             M = fmax(M, sRunM[v][p]);
         double S = 0.0;
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < NW; ++v)
             if (sRunM[v][p] > -INFINITY)
                 S += sRunS[v][p] * (double)fast_exp2((float)(sRunM[v][p] - M));
         const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_parts + blockIdx.x;
@@ -704,29 +742,36 @@ hipError_t launch_logit_sum(const ScoreArgs &a, int pt, dim3 grid, hipStream_t s
 
 // The softmax-mode kernel, instantiated for the pair counts of one group.  Its grid is one
 // resident round: as many workgroups per CU as the variant's registers and LDS allow (asked
-// of the runtime once per variant), each streaming a run of tiles.  a.n_parts comes in as
-// the workspace's maximum and leaves as the count launched (the finalize reads that many).
+// of the runtime once per variant), each taking an equal share of its stream's tiles.
+// a.n_parts comes in as the workspace's maximum and leaves as the count launched (the
+// finalize reads that many).
+template <int D, int PC, bool FLAT>
+hipError_t launch_prob_variant(ScoreArgs &a, int cus, hipStream_t st)
+{
+    constexpr int nt = 64 * prob_waves<D, PC>();
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, srh_prob_logits_kernel<D, PC, FLAT>, nt, 0) !=
+                hipSuccess ||
+            n < 1)
+            n = 1;
+        return n;
+    }();
+    const int ws = a.n_groups * a.B;
+    a.n_parts = std::max(1, std::min(a.n_parts, (per_cu * cus + ws - 1) / ws));
+    const dim3 grid((unsigned)a.n_parts, (unsigned)a.n_groups, (unsigned)a.B);
+    hipLaunchKernelGGL((srh_prob_logits_kernel<D, PC, FLAT>), grid, dim3(nt), 0, st, a);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_prob(ScoreArgs &a, int max_pairs, int cus, hipStream_t st)
 {
     bool flat = true;
     for (int g = 0; g < a.n_groups; ++g)
         flat = flat && !a.grp[g].k.pt && a.grp[g].k.st >= 0 && a.grp[g].k.st * 2 < (int64_t)1 << 32;
-    auto go = [&](auto kern) {
-        static const int per_cu = [&] {
-            int n = 0;
-            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, kThreads, 0) != hipSuccess || n < 1)
-                n = 1;
-            return n;
-        }();
-        const int ws = a.n_groups * a.B;
-        a.n_parts = std::max(1, std::min(a.n_parts, (per_cu * cus + ws - 1) / ws));
-        const dim3 grid((unsigned)a.n_parts, (unsigned)a.n_groups, (unsigned)a.B);
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, st, a);
-        return hipGetLastError();
-    };
-#define DUSTIN_PROB(PCV)                                                              \
-    return flat ? go(srh_prob_logits_kernel<D, PCV, true>) : go(srh_prob_logits_kernel<D, PCV, false>)
+#define DUSTIN_PROB(PCV) \
+    return flat ? launch_prob_variant<D, PCV, true>(a, cus, st) : launch_prob_variant<D, PCV, false>(a, cus, st)
     if (max_pairs <= 4)
         DUSTIN_PROB(4);
     if (max_pairs <= 5)
