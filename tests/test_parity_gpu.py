@@ -254,3 +254,29 @@ def test_k_and_v_at_different_row_offsets():
         step.dense(0)
         torch.cuda.synchronize()
         check_attn(step.out, step.lse, refd, bs, f"dense, {name}")
+
+
+def test_step_replayed_as_hip_graph_matches_eager():
+    """The whole step (both scoring calls, selection, two attention layers) captured once as
+    a HIP graph: every replay, with eager work and synchronisations in between, gives
+    bitwise the eager results (no call records a memset or allocates)."""
+    inp = W.make_inputs(W.QWEN7B, device="cuda", target_layers=[0, 1])
+    step = step_for(inp, [0, 1])
+    outs = lambda: [t.clone() for t in (step.score_draft, step.score_target, step.idx, step.count, step.out,
+                                        step.lse)]
+    step.step()
+    torch.cuda.synchronize()
+    ref = outs()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step.step()
+    for r in range(3):
+        for t in (step.score_draft, step.score_target, step.out, step.lse):
+            t.zero_()                         # eager work between the replays
+        step.idx.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs(), ref):
+            assert torch.equal(a, b), f"replay {r} differs from the eager step"
+    say("  three graph replays equal the eager step bitwise")
