@@ -167,8 +167,10 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC>() / 4)))) void srh_prob_lo
     // then feeds four tokens), 2 for the 128-wide rows (two tiles of them are in flight)
     constexpr int S = (D > 64 || PC > 8) ? 2 : 4;
     constexpr int KT = S;                  // tokens converted to fp64 at once
-    // tiles in flight in registers: two where the registers hold them (row addresses are
-    // then one multiply-add each), else one
+    // tiles in flight in registers per wave: two where the registers hold them (row
+    // addresses are then one multiply-add each), else one.  Four 8 KB tiles fit the
+    // matrix-core variant at head dim 64 but measured slower: they only lengthen the queue
+    // of requests every wave issues at the start.
     constexpr int kDepth = (FLAT && (D == 64 || PC <= 5)) ? 2 : 1;
     constexpr int RB = D * 2;          // bytes per key row
     constexpr int RSTR = RB + 16;      // LDS row stride (conflict-free 16-byte row reads)
@@ -454,52 +456,36 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC>() / 4)))) void srh_prob_lo
     };
     // Tiles are claimed one at a time from the workgroup's counter, so a wave that gets
     // less of the SIMDs than its neighbours simply takes fewer tiles.  A wave's claims
-    // increase, so the loop ends at the first claim past the share (single exit: the
-    // compiler's waits then keep the second tile in flight).
+    // increase, so the loop ends at the first claim past the share, and every later buffer
+    // of the round holds a tile past it too (single exit: the compiler's waits then keep
+    // the other kDepth-1 tiles in flight).
     auto claim = [&]() {
         int v = 0;
         if (lane == 0)
             v = atomicAdd(&sNext, 1);
         return q_lo + __builtin_amdgcn_readfirstlane(v);
     };
-    int qa = claim();
-    u32x4 krA[LPT];
-    issue(krA, qa);
-    if constexpr (kDepth == 2) {
-        int qb = claim();
-        u32x4 krB[LPT];
-        __builtin_amdgcn_sched_barrier(0);   // krA's loads first, as in the loop
-        issue(krB, qb);
-        while (qa < q_hi) {
-            stage(krA);
-            const int qc = claim();
-            issue(krA, qc);
-            if constexpr (MF)
-                process_mf(qa);
-            else
-                process(qa);
-            stage(krB);
-            const int qd = claim();
-            issue(krB, qd);
-            if (qb < q_hi) {
+    int qs[kDepth];
+    u32x4 kr[kDepth][LPT];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+        qs[d] = claim();
+        __builtin_amdgcn_sched_barrier(0);   // tile d's loads after tile d-1's, as in the loop
+        issue(kr[d], qs[d]);
+    }
+    while (qs[0] < q_hi) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            stage(kr[d]);
+            const int nq = claim();
+            issue(kr[d], nq);
+            if (d == 0 || qs[d] < q_hi) {
                 if constexpr (MF)
-                    process_mf(qb);
+                    process_mf(qs[d]);
                 else
-                    process(qb);
+                    process(qs[d]);
             }
-            qa = qc;
-            qb = qd;
-        }
-    } else {
-        while (qa < q_hi) {
-            stage(krA);
-            const int qc = claim();
-            issue(krA, qc);
-            if constexpr (MF)
-                process_mf(qa);
-            else
-                process(qa);
-            qa = qc;
+            qs[d] = nq;
         }
     }
     {
