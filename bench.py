@@ -20,6 +20,8 @@ since those counters were taken.
 `--counters` runs only a calibration copy and the attention calls, for counter passes.
 `--estimator-sweep` times the naive all-heads estimator, dense attention and the SRH
 scoring at contexts 1k..64k instead of the step (one JSON line of its own).
+`--sweep` times sparse against dense attention (and each point's scoring and selection)
+on one 72B-shaped layer at batch 64 over budgets 1024..4096 and gamma 2..8.
 """
 from __future__ import annotations
 
@@ -92,6 +94,8 @@ def main():
     ap.add_argument("--counters", action="store_true", help="calibration copy + attention calls only")
     ap.add_argument("--estimator-sweep", action="store_true",
                     help="naive all-heads estimator vs dense attention vs SRH scoring, context 1k..64k")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one 72B-shaped layer at B=64, 32k: sparse vs dense attention per (budget, gamma)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -107,6 +111,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.estimator_sweep:
         estimator_sweep(dev, args)
+        return
+    if args.sweep:
+        attention_sweep(dev, args)
         return
     w = W.QWEN72B
     if args.layers != w.target.layers:
@@ -313,6 +320,72 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, step, args.cpu_seconds, b_attn, b_score, b_select, attn_layers)
     print(json.dumps(line), flush=True)
+
+
+def attention_sweep(dev, args):
+    """Sparse against dense verification attention on one Qwen2.5-72B-shaped layer at batch
+    64 and 32k context, for budgets 1024/2048/4096 and gamma 2/4/8 (m = budget/4; the draft
+    tier's size does not change the attention's cost), plus each point's scoring and
+    selection.  Two copies of the layer's caches alternate, so no call finds the previous
+    call's rows in the last-level cache.  Prints one JSON line."""
+    import torch
+
+    from sparse_kv_attention_amd import workloads as W
+    from sparse_kv_attention_amd.pipeline import SparseVerifyStep
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    points = []
+    for gamma in (2, 4, 8):
+        base = W.sweep_point(1024, gamma, 0.25)
+        w2 = W.shrink(base, target=W.ModelShape(2, 64, 8, 128), srh_target=tuple((0, h) for _, h in base.srh_target))
+        inp = W.make_inputs(w2, device=dev)             # layers 0 and 1: identical shapes, different data
+        T = w2.target
+        for k in (1024, 2048, 4096):
+            for r in (0.25, 0.5):
+                wk = W.shrink(w2, budget=k, n_window=k // 8, m=int(r * k))
+                inp.w = wk
+                inp.budget.fill_(k)
+                inp.n_window.fill_(k // 8)
+                inp.m.fill_(int(r * k))
+                inp.k_max = k
+                step = SparseVerifyStep(inp, layers=[0, 1])
+                step.score()
+                step.select()
+                us_score = timed(step.score, 5)
+                us_select = timed(step.select, 10)
+                if r != 0.25:
+                    points.append({"budget": k, "gamma": gamma, "m_over_budget": r, "score_us": round(us_score, 1),
+                                   "select_us": round(us_select, 1)})
+                    continue
+                counts = step.count.cpu().tolist()
+                us_sparse = timed(lambda: (step.attn(0), step.attn(1)), 10) / 2
+                us_dense = timed(lambda: (step.dense(0), step.dense(1)), 3) / 2
+                b_sp = attn_bytes(w2.batch, T.hq, T.hkv, T.d, w2.n_verify, counts)
+                b_de = attn_bytes(w2.batch, T.hq, T.hkv, T.d, w2.n_verify, [inp.n_max] * w2.batch) - w2.batch * inp.n_max * 4
+                points.append({"budget": k, "gamma": gamma, "m_over_budget": r, "score_us": round(us_score, 1),
+                               "select_us": round(us_select, 1), "sparse_attn_us": round(us_sparse, 2),
+                               "sparse_attn_gbs": round(b_sp / (us_sparse * 1e-6) / 1e9, 1),
+                               "dense_attn_us": round(us_dense, 2), "dense_attn_gbs": round(b_de / (us_dense * 1e-6) / 1e9, 1),
+                               "attn_speedup": round(us_dense / us_sparse, 2), "byte_ratio": round(b_de / b_sp, 2)})
+                print(f"# {points[-1]}", file=sys.stderr, flush=True)
+                del step
+        del inp
+        torch.cuda.empty_cache()
+    print(json.dumps({"attention_sweep": points, "batch": 64, "ctx": 32768,
+                      "layer": "64 q-heads / 8 KV heads, d 128, bf16",
+                      "inputs": "N(0,1) with Pareto(1.2) key-norm salience capped at 16"}), flush=True)
 
 
 def estimator_sweep(dev, args):
