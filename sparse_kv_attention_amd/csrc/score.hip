@@ -144,22 +144,23 @@ __device__ __forceinline__ double quad_xor(double v)
 
 // Waves per workgroup of the softmax-mode logit kernel.  One workgroup fills a CU, so all
 // of a CU's waves draw tiles from one counter and none is left running alone at the end.
-// Groups of more than 8 pairs need a lane's whole register file (one wave per SIMD), the
-// others run two waves per SIMD (three, possible for the 140-register matrix-core variant,
-// measured slower: the third wave's tiles only add to the requests queued at the start).
-template <int D, int PC>
+// Two waves per SIMD fit every variant's registers but the paged one for groups of more
+// than 8 pairs at head dim 128, which would spill and runs one wave per SIMD instead.
+// (Three per SIMD, possible for the 140-register matrix-core variant, measured slower:
+// the third wave's tiles only add to the requests queued at the start.)
+template <int D, int PC, bool FLAT>
 constexpr int prob_waves()
 {
-    return PC > 8 ? 4 : 8;
+    return (PC > 8 && D == 128 && !FLAT) ? 4 : 8;
 }
 
 // FLAT: every group's view is unpaged with a row stride below 4 GiB, so a row address is a
 // per-workgroup base plus token x stride (one 32x32->64 multiply-add per load).
 template <int D, int PC, bool FLAT>
-__global__ __launch_bounds__((64 * prob_waves<D, PC>()))
-__attribute__((amdgpu_waves_per_eu((prob_waves<D, PC>() / 4)))) void srh_prob_logits_kernel(ScoreArgs a)
+__global__ __launch_bounds__((64 * prob_waves<D, PC, FLAT>()))
+__attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_prob_logits_kernel(ScoreArgs a)
 {
-    constexpr int NW = prob_waves<D, PC>();
+    constexpr int NW = prob_waves<D, PC, FLAT>();
     constexpr int NT = 64 * NW;
     // groups of 4 pairs: the dot products run on the fp64 matrix cores
     constexpr bool MF = PC == 4;
@@ -734,7 +735,7 @@ hipError_t launch_logit_sum(const ScoreArgs &a, int pt, dim3 grid, hipStream_t s
 template <int D, int PC, bool FLAT>
 hipError_t launch_prob_variant(ScoreArgs &a, int cus, hipStream_t st)
 {
-    constexpr int nt = 64 * prob_waves<D, PC>();
+    constexpr int nt = 64 * prob_waves<D, PC, FLAT>();
     static const int per_cu = [] {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, srh_prob_logits_kernel<D, PC, FLAT>, nt, 0) !=
