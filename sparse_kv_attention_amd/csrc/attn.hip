@@ -117,14 +117,15 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
     int64_t *sOffV = a.kv_same ? sOffK : sOffK + kSplitMax / 2;
 
     // ---- block -> (sequence, KV head, query group, split).  Every workgroup of one
-    //      (sequence, KV head) has the same blockIdx % 8, i.e. runs on the same XCD, so
-    //      the query groups re-reading its rows find them in that XCD's L2 ----
+    //      (sequence, KV head) has the same blockIdx % 8, i.e. runs on the same XCD, and
+    //      the query groups of one split are dispatched back to back, so the groups
+    //      re-reading a split's rows find them in that XCD's L2 ----
     const int x = blockIdx.x;
     const int hi = x >> 3;
-    const int split = hi % a.splits;
-    const int t2 = hi / a.splits;
-    const int qg = t2 % a.qgroups;
-    const int bg = (t2 / a.qgroups) * 8 + (x & 7);
+    const int qg = hi % a.qgroups;
+    const int t2 = hi / a.qgroups;
+    const int split = t2 % a.splits;
+    const int bg = (t2 / a.splits) * 8 + (x & 7);
     if (bg >= a.B * a.Hkv)
         return;
     const int pair = bg * a.qgroups + qg;
