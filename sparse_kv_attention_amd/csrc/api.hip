@@ -188,7 +188,7 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
 
 struct ScoreWs {
     int n_pad, n_tiles, n_parts, total_pairs, logit_rows;
-    size_t logits_off, max_off, pmax_off, psum_off, bytes;
+    size_t logits_off, max_off, tsum_off, pmax_off, psum_off, bytes;
 };
 
 int pairs_per_qhead(int n_q, int mode) { return mode == DUSTIN_SCORE_LOGIT_SUM2 ? std::min(2, n_q) : n_q; }
@@ -214,7 +214,8 @@ ScoreWs score_workspace(int B, int n_max, int total_qheads, int n_q, int mode)
     const size_t parts = prob ? (size_t)B * w.total_pairs * w.n_parts : 0;
     w.logits_off = 0;
     w.max_off = align_up(sizeof(float) * (size_t)B * w.logit_rows * w.n_pad);
-    w.pmax_off = w.max_off + align_up(sizeof(double) * stats);
+    w.tsum_off = w.max_off + align_up(sizeof(double) * stats);
+    w.pmax_off = w.tsum_off + align_up(sizeof(double) * stats);
     w.psum_off = w.pmax_off + align_up(sizeof(double) * parts);
     w.bytes = w.psum_off + align_up(sizeof(double) * parts);
     return w;
@@ -296,6 +297,7 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
     a.mul = mode == DUSTIN_SCORE_PROB_SUM ? (double)scale * 1.4426950408889634 : (double)scale;
     a.logits = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.logits_off);
     a.tile_max = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.max_off);
+    a.tile_sum = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.tsum_off);
     a.part_max = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.pmax_off);
     a.part_sum = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.psum_off);
     a.score = score;

@@ -68,6 +68,7 @@ struct ScoreArgs {
     float *logits;           // [B][logit_rows][n_pad]: PROB_SUM l - tile max per pair; logit-sum
                              //   modes: per group, the sum of its pairs' logits
     double *tile_max;        // PROB_SUM: [B][total_pairs][n_tiles], n_tiles = ceil(n_max / kStatTile)
+    double *tile_sum;        // PROB_SUM: [B][total_pairs][n_tiles], sum of exp2(l - tile max)
     double *part_max;        // PROB_SUM: [B][total_pairs][n_parts], one (max, sum of exp2(l - max))
     double *part_sum;        //   per workgroup of the logit kernel
     float *score;            // [B][n_max]

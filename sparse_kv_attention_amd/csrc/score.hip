@@ -18,8 +18,8 @@
 //                    of their 64-token statistics tile (one wave), so tokens near the
 //                    maximum — the ones that carry probability mass — keep full relative
 //                    precision even when logits are large.  Every tile leaves its maximum
-//                    per pair; every workgroup leaves one (max, sum of exp2) per pair over
-//                    all its tiles.
+//                    and sum of exp2 per pair; every workgroup folds its tiles, in tile
+//                    order, into one (max, sum of exp2) per pair.
 //   srh_finalize     one workgroup per (1024 tokens, sequence): per pair, the global max
 //                    and 1/Z from the workgroup partials (one wave per pair, loads of
 //                    several pairs in flight together), then per token the sum over pairs
@@ -179,8 +179,6 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_p
     constexpr int LPT = kStatTile * CPR / 64;   // 16-byte loads per lane per 64-token tile
     __shared__ __align__(16) uint8_t sK[NW][kStatTile * RSTR];   // one tile per wave
     __shared__ __align__(16) double sQ[PC][D];
-    __shared__ double sRunM[NW][PC];   // per wave: running max and sum of exp2(l - max)
-    __shared__ double sRunS[NW][PC];
     __shared__ int sNext;              // tiles claimed so far by the workgroup's waves
 
     const ScoreGroup &G = a.grp[blockIdx.y];
@@ -208,9 +206,6 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_p
         }
         return;
     }
-    // running (max, sum of exp2(l - max)) of the wave's tiles: lane p holds pair p
-    double runM = -INFINITY, runS = 0.0;
-
     // the group's queries (fp64) stay in LDS for every tile of this workgroup
     for (int e = tid; e < PC * D; e += NT) {
         const int p = e / D;
@@ -360,22 +355,16 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_p
         for (int p = 0; p < PC; ++p)
             if (p < G.n_pairs && valid)
                 a.logits[(row0 + p) * a.n_pad + tok] = off[p];
-        // lane p < PC takes pair p: it stores the tile maximum and folds the tile into its
-        // running (max, sum)
+        // lane p < PC takes pair p: it stores the tile's maximum and sum of exp2
         float m_l = mf[0], s_l = ex[0];
 #pragma unroll
         for (int p = 1; p < PC; ++p) {
             m_l = lane == p ? mf[p] : m_l;
             s_l = lane == p ? ex[p] : s_l;
         }
-        if (lane < G.n_pairs && lane < PC && stile < a.n_tiles)
+        if (lane < G.n_pairs && lane < PC && stile < a.n_tiles) {
             a.tile_max[(row0 + lane) * a.n_tiles + stile] = (double)m_l;
-        if (m_l > -INFINITY) {
-            const double m = (double)m_l;
-            const double M1 = fmax(runM, m);
-            const double s0 = runM > -INFINITY ? runS * (double)fast_exp2((float)(runM - M1)) : 0.0;
-            runS = s0 + (double)s_l * (double)fast_exp2((float)(m - M1));
-            runM = M1;
+            a.tile_sum[(row0 + lane) * a.n_tiles + stile] = (double)s_l;
         }
     };
 
@@ -444,15 +433,10 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_p
             for (int g = 0; g < 4; ++g)
                 if (tok0 + 16 * g < N)
                     a.logits[(row0 + pr) * a.n_pad + tok0 + 16 * g] = off[g];
-            if (t16 == 0 && stile < a.n_tiles)
+            if (t16 == 0 && stile < a.n_tiles) {
                 a.tile_max[(row0 + pr) * a.n_tiles + stile] = (double)mx;
-        }
-        if (mx > -INFINITY) {
-            const double m = (double)mx;
-            const double M1 = fmax(runM, m);
-            const double s0 = runM > -INFINITY ? runS * (double)fast_exp2((float)(runM - M1)) : 0.0;
-            runS = s0 + (double)red[0] * (double)fast_exp2((float)(m - M1));
-            runM = M1;
+                a.tile_sum[(row0 + pr) * a.n_tiles + stile] = (double)red[0];
+            }
         }
     };
     // Tiles are claimed one at a time from the workgroup's counter, so a wave that gets
@@ -489,30 +473,33 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_p
             qs[d] = nq;
         }
     }
-    {
-        // the lane holding pair p's running (max, sum): lane p, or lane 16p on the
-        // matrix-core path
-        const int p_own = !MF ? (lane < PC ? lane : -1) : ((lane & 15) == 0 ? lane >> 4 : -1);
-        if (p_own >= 0) {
-            sRunM[w][p_own] = runM;
-            sRunS[w][p_own] = runS;
+    // This workgroup's (max, sum of exp2(l - max)) per pair over its tiles, folded in a
+    // fixed order whichever wave took a tile, so the result does not depend on the claims:
+    // one wave per pair, lane i folding tiles q_lo + i, q_lo + i + 64, ... in order (both
+    // values of a tile requested together), then the lanes combined by a fixed butterfly.
+    __syncthreads();                  // every tile's (max, sum) is stored
+    for (int p = w; p < G.n_pairs; p += NW) {
+        const int64_t row = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_tiles;
+        double Ml = -INFINITY, Sl = 0.0;
+        for (int t = q_lo + lane; t < q_hi; t += 64) {
+            const double m = a.tile_max[row + t], sm = a.tile_sum[row + t];
+            if (m > -INFINITY) {
+                const double M1 = fmax(Ml, m);
+                Sl = (Ml > -INFINITY ? Sl * (double)fast_exp2((float)(Ml - M1)) : 0.0) +
+                     sm * (double)fast_exp2((float)(m - M1));
+                Ml = M1;
+            }
         }
-    }
-    __syncthreads();
-    if (tid < G.n_pairs) {   // this workgroup's (max, sum) per pair, over its waves
-        const int p = tid;
-        double M = -INFINITY;
+        const double M = wave_max_f64_dpp(Ml);
+        double S = Ml > -INFINITY ? Sl * (double)fast_exp2((float)(Ml - M)) : 0.0;
 #pragma unroll
-        for (int v = 0; v < NW; ++v)
-            M = fmax(M, sRunM[v][p]);
-        double S = 0.0;
-#pragma unroll
-        for (int v = 0; v < NW; ++v)
-            if (sRunM[v][p] > -INFINITY)
-                S += sRunS[v][p] * (double)fast_exp2((float)(sRunM[v][p] - M));
-        const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_parts + blockIdx.x;
-        a.part_max[e] = M;
-        a.part_sum[e] = S;
+        for (int o = 32; o > 0; o >>= 1)
+            S += __shfl_xor(S, o);
+        if (lane == 0) {
+            const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_parts + blockIdx.x;
+            a.part_max[e] = M;
+            a.part_sum[e] = S;
+        }
     }
 }
 

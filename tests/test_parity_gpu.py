@@ -280,3 +280,24 @@ def test_step_replayed_as_hip_graph_matches_eager():
         for a, b in zip(outs(), ref):
             assert torch.equal(a, b), f"replay {r} differs from the eager step"
     say("  three graph replays equal the eager step bitwise")
+
+
+def test_scores_repeat_bitwise():
+    """The waves of a scoring workgroup claim tiles dynamically, but each workgroup folds
+    its tiles' statistics in tile order: repeated calls give bitwise the same scores."""
+    w = W.shrink(W.QWEN7B, batch=3, n_ctx=5000, ragged_lo=1000)
+    inp = W.make_inputs(w, device="cuda", target_layers=[0])
+    step = step_for(inp, [0])
+    first = None
+    for r in range(4):
+        step.score_draft.zero_()
+        step.score_target.zero_()
+        step.score()
+        torch.cuda.synchronize()
+        got = (step.score_draft.clone(), step.score_target.clone())
+        if first is None:
+            first = got
+            check_scores(got[1].cpu().numpy(), oracle_scores(inp, "target", O.PROB_SUM, [0, 1, 2]), "target scores")
+        else:
+            assert torch.equal(got[0], first[0]) and torch.equal(got[1], first[1]), f"call {r} differs"
+    say("  four scoring calls bitwise equal")
