@@ -216,3 +216,26 @@ def test_all_heads_estimator_widest_groups():
                 O.score_stream(K, u16(cq[:, h:h + nh]), ctx, est.n_max, 1.0 / math.sqrt(shape.d), O.PROB_SUM, acc)
                 h += nh
             check_scores(got.cpu().numpy(), acc, f"{name} all-heads call")
+
+
+def test_all_heads_estimator_paged():
+    """The estimator's widest groups on a paged, ragged cache: the page-table variant of the
+    16-pair softmax kernel (one wave per SIMD at head dim 128) against the oracle."""
+    from sparse_kv_attention_amd.pipeline import AllHeadsEstimator
+    from sparse_kv_attention_amd.workloads import logical_rows
+    w = W.shrink(W.RAGGED_PAGED, batch=3, n_ctx=3000, ragged_lo=900, target=W.ModelShape(1, 64, 8, 128),
+                 srh_target=((0, 0),))
+    inp = W.make_inputs(w, device="cuda")
+    ctx = inp.ctx_len.cpu().numpy()
+    q = inp.q_verify[0].permute(0, 2, 1, 3).contiguous()
+    est = AllHeadsEstimator(inp.k_cache[0], inp.page_table, q, w.target.hkv, inp.ctx_len, 1.0 / math.sqrt(128))
+    est.score()
+    torch.cuda.synchronize()
+    K_all = np.stack([u16(logical_rows(inp, inp.k_cache[0], b, est.n_max)) for b in range(w.batch)])
+    for (groups, cq), got in zip(est.calls, est.scores):
+        acc = np.zeros((w.batch, est.n_max))
+        h = 0
+        for _, g, nh in groups:
+            O.score_stream(K_all[:, :, g], u16(cq[:, h:h + nh]), ctx, est.n_max, 1.0 / math.sqrt(128), O.PROB_SUM, acc)
+            h += nh
+        check_scores(got.cpu().numpy(), acc, "paged all-heads call")
