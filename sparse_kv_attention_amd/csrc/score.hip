@@ -600,13 +600,14 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
     }
 }
 
-constexpr int kFinTokens = 1024;
+constexpr int kFinTokens = 1024;          // = kThreads * 4: every thread sums four tokens
 constexpr int kFinTiles = kFinTokens / kStatTile;
 constexpr int kFinBatch = 8;
 constexpr int kFinChunk = 32;              // pairs whose logits one finalize thread holds at once               // pairs per wave whose loads are in flight together
 
 __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
 {
+    static_assert(kFinTokens == 4 * kThreads, "one f32x4 of tokens per thread");
     __shared__ float sOff[kMaxGroups * kMaxProbPairsPerGroup][kFinTiles];
     __shared__ float sInvZ[kMaxGroups * kMaxProbPairsPerGroup];
     const int b = blockIdx.y;
