@@ -136,6 +136,12 @@ def test_commit():
     D.dustin_kv_commit(torch.from_numpy(bad).cuda(), c_dev, n_new)
     torch.cuda.synchronize()
     assert np.array_equal(c_dev.cpu().numpy(), O.kv_commit([10] * 4, np.clip(bad, 0, n_new - 1), n_new))
+    # out-of-range lengths act as their clamped values, [0, 2^30]
+    lens = np.array([-5, 2 ** 31 - 1, 0, 2 ** 30], np.int32)
+    c_dev = torch.from_numpy(lens).cuda()
+    D.dustin_kv_commit(torch.tensor([1, 2, 3, 4], dtype=torch.int32, device="cuda"), c_dev, n_new)
+    torch.cuda.synchronize()
+    assert np.array_equal(c_dev.cpu().numpy(), O.kv_commit(np.clip(lens, 0, 2 ** 30), [1, 2, 3, 4], n_new))
 
 
 def check_recovery(inp, layer, bsel, heads=None):
