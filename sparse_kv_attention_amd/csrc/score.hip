@@ -233,11 +233,15 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_p
     const uint32_t flat_st = (uint32_t)(G.k.st * 2);
     auto issue = [&](u32x4 (&kr)[LPT], int tile) {
         const int t0 = tile * kStatTile;
+        // a tile past the share (the last claims of every wave) reads row N-1 only: its
+        // rows may be live rows of the next workgroup's share, which would then be fetched
+        // twice
+        const bool mine = tile < q_hi;
 #pragma unroll
         for (int i = 0; i < LPT; ++i) {
             const int c = lane + i * 64;
             const int r = c / CPR;
-            const int t = min(t0 + r, N - 1);
+            const int t = mine ? min(t0 + r, N - 1) : N - 1;
             const u32x4 *src;
             if constexpr (FLAT)
                 src = reinterpret_cast<const u32x4 *>(flat_base + (uint64_t)(uint32_t)t * flat_st);
