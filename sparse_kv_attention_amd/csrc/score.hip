@@ -757,6 +757,8 @@ hipError_t launch_prob(ScoreArgs &a, int max_pairs, int cus, hipStream_t st)
         DUSTIN_PROB(5);
     if (max_pairs <= 8)
         DUSTIN_PROB(8);
+    if (max_pairs <= 12)
+        DUSTIN_PROB(12);
     if (max_pairs <= 16)
         DUSTIN_PROB(16);
 #undef DUSTIN_PROB
