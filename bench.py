@@ -255,10 +255,18 @@ def main():
         torch.cuda.synchronize()
         recovery[f"layer_{l}"] = {"mean": round(float(r.mean()), 5), "min": round(float(r.min()), 5),
                                   "max": round(float(r.max()), 5)}
+    # the Vegas aggregate in its literal form: the first and bonus verify queries of every
+    # query head of one layer (a logit-sum call over the layer's 8 KV heads)
+    vg_score = torch.zeros((B, inp.n_max), dtype=torch.float32, device=dev)
+    vg_ws = step.vegas_all_heads(attn_layers[0], vg_score)
+    us_vegas_all = timed(lambda: step.vegas_all_heads(attn_layers[0], vg_score, vg_ws), reps)
+    b_vegas_all = score_bytes(B, inp.n_max, [T.d] * T.hkv, 1)
     # the whole step captured once as a HIP graph and replayed (same kernels, same order)
     us_step_graph = graph_timed(step.step, n_calls=1, replays=args.steps)
     us_attn_graph = graph_timed(lambda: [step.attn(l) for l in attn_layers], n_calls=1, replays=reps) / len(attn_layers)
     step_extras = {
+        "vegas_all_heads_layer_score_us": round(us_vegas_all, 2),
+        "vegas_all_heads_layer_score_gbs": round(b_vegas_all / (us_vegas_all * 1e-6) / 1e9, 1),
         "step_us_graph_replay": round(us_step_graph, 1),
         "attn_per_call_graph_replay_us": round(us_attn_graph, 2),
         "kv_write_block_us": round(us_write, 2),

@@ -97,6 +97,23 @@ class SparseVerifyStep:
                             self.scale, self.out if out is None else out, self.lse if lse is None else lse,
                             self.ws_attn, stream)
 
+    def vegas_all_heads(self, layer: int, score, ws=None, all_queries: bool = False, stream=None):
+        """The Vegas aggregate as the German Vegas summary writes it (2A: logits summed over
+        every query head; 2B: the first and the bonus query only, unless all_queries): one
+        logit-sum scoring call over every KV head of a target layer with all of its query
+        heads, from the layer's verify queries.  Writes score [B][n_max]; returns the
+        workspace it used (pass it back to reuse it)."""
+        inp = self.inp
+        q = inp.q_verify[layer].permute(0, 2, 1, 3).contiguous()      # [B][Hq][n_verify][d]
+        k, _ = self.kv[layer]
+        groups = [(k, g, self.T.group) for g in range(self.T.hkv)]
+        mode = D.SCORE_LOGIT_SUM_ALL if all_queries else D.SCORE_LOGIT_SUM2
+        if ws is None:
+            ws = D.workspace(D.dustin_srh_score_workspace_size(self.B, self.n_max, self.T.hq, inp.w.n_verify, mode),
+                             score.device)
+        D.dustin_srh_score(inp.ctx_len, groups, q, self.scale, mode, score, ws, stream)
+        return ws
+
     def recovery(self, layer: int, rec=None, stream=None):
         """Share of the dense attention mass on the kept set, per (b, h, t) [B][Hq][n_verify]:
         one sparse and one dense call on the layer, then the library's recovery kernel."""

@@ -245,3 +245,39 @@ def test_all_heads_estimator_paged():
             O.score_stream(K_all[:, :, g], u16(cq[:, h:h + nh]), ctx, est.n_max, 1.0 / math.sqrt(128), O.PROB_SUM, acc)
             h += nh
         check_scores(got.cpu().numpy(), acc, "paged all-heads call")
+
+
+@pytest.mark.parametrize("all_queries", [False, True])
+def test_vegas_aggregate_over_every_head_of_a_layer(all_queries):
+    """The Vegas aggregate in its literal form (German Vegas summary 2A/2B): logits of the
+    first and bonus verify queries (or all of them) summed over all 64 query heads of one
+    target layer, on a ragged paged cache; then pure top-k selection, bit-exact."""
+    w = W.shrink(W.RAGGED_PAGED, batch=3, n_ctx=4000, ragged_lo=1200, target=W.ModelShape(1, 64, 8, 128),
+                 srh_target=((0, 0),))
+    inp = W.make_inputs(w, device="cuda")
+    step = SparseVerifyStep(inp, layers=[0], logit_sum2=True)
+    step.vegas_all_heads(0, step.score_target, all_queries=all_queries)
+    step.select()
+    torch.cuda.synchronize()
+    ctx = inp.ctx_len.cpu().numpy()
+    n = inp.n_max
+    q = inp.q_verify[0].permute(0, 2, 1, 3).contiguous()
+    mode = O.LOGIT_SUM_ALL if all_queries else O.LOGIT_SUM2
+    acc = np.zeros((w.batch, n))
+    cond = np.zeros((w.batch, n))
+    G = w.target.group
+    js = list(range(w.n_verify)) if all_queries else [0, w.n_verify - 1]
+    for g in range(w.target.hkv):
+        Kg = np.stack([u16(rows(inp, inp.k_cache[0], b, n)[:, g]) for b in range(w.batch)])
+        O.score_stream(Kg, u16(q[:, g * G:(g + 1) * G]), ctx, n, 1.0 / math.sqrt(128), mode, acc)
+        for b in range(w.batch):
+            Kd = rows(inp, inp.k_cache[0], b, n)[:, g].double().cpu()
+            Qd = q[b, g * G:(g + 1) * G][:, js].double().cpu().reshape(-1, 128)
+            cond[b] += (Kd @ Qd.T).abs().sum(1).numpy() / math.sqrt(128)
+    got = step.score_target.cpu().numpy()
+    check_scores(got, acc, "all-heads Vegas aggregate", cond=cond)
+    zeros = np.zeros(w.batch, np.int32)
+    idx_o, cnt_o = O.select(ctx, None, got.astype(np.float64), inp.budget.cpu().numpy(), zeros, zeros, zeros,
+                            inp.k_max)
+    assert np.array_equal(step.count.cpu().numpy(), cnt_o)
+    assert np.array_equal(step.idx.cpu().numpy()[:, :inp.k_max], idx_o)
