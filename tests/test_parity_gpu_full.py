@@ -28,10 +28,16 @@ def test_qwen72b_b8_n32768_sampled():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("k,g,r", [(1024, 2, 0.25), (2048, 4, 0.5), (4096, 8, 0.5)])
+DENSE_POINTS = {(1024, 2, 0.25), (2048, 4, 0.5), (4096, 8, 0.5)}
+
+
+@pytest.mark.parametrize("k,g,r", [(k, g, r) for k in (1024, 2048, 4096) for g in (2, 4, 8) for r in (0.25, 0.5)])
 def test_sweep_b64_point(k, g, r):
+    # every point of the budget x gamma x m/budget grid; dense attention at one point per
+    # budget and gamma class
     inp = W.make_inputs(W.sweep_point(k, g, r), device="cuda")
-    check_pipeline(inp, [0], [0], b_attn=[0, 63], b_score=[0, 31, 63], b_dense=[0])
+    dense = (k, g, r) in DENSE_POINTS
+    check_pipeline(inp, [0], [0] if dense else [], b_attn=[0, 63], b_score=[0, 31, 63], b_dense=[0])
     del inp
     torch.cuda.empty_cache()
 
