@@ -65,3 +65,24 @@ def test_ragged_paged_logit_sum2_topk(paged):
 def test_ragged_paged_logit_sum_all_topk(paged):
     ctx = paged.ctx_len.cpu().numpy()
     check_pipeline(paged, [0], [], b_attn=[int(np.argmin(ctx))], b_score=[1, 8, 14], logit_sum_all=True)
+
+
+def test_qwen72b_every_layer():
+    """All 80 layers resident (each with its own caches, as the bench runs them): sparse
+    attention of every layer for sequence 0, and of layers 0, 40 and 79 for every sequence,
+    against the oracle, on the GPU's own selection."""
+    from _harness import check_attn, oracle_attn
+    from sparse_kv_attention_amd.pipeline import SparseVerifyStep
+    inp = W.make_inputs(W.QWEN72B, device="cuda")
+    step = SparseVerifyStep(inp)
+    step.score()
+    step.select()
+    torch.cuda.synchronize()
+    idx, cnt = step.idx.cpu().numpy(), step.count.cpu().numpy()
+    for l in range(inp.w.target.layers):
+        step.attn(l)
+        torch.cuda.synchronize()
+        bsel = list(range(inp.w.batch)) if l in (0, 40, 79) else [0]
+        check_attn(step.out, step.lse, oracle_attn(inp, l, idx, cnt, bsel), bsel, f"layer {l}")
+    del step, inp
+    torch.cuda.empty_cache()
