@@ -101,7 +101,12 @@ struct AttnShape {
     static constexpr int ACC = G::DVT * QT * 4; // O accumulator floats per lane
     static constexpr int TAB = (kSplitMax + 32) * 8;   // + the new-token rows' K and V offsets
     static constexpr int RING = 4 * R * G::SLOT;
-    static constexpr int MRG = 4 * 64 * ACC * 4 + 2 * 4 * QR * 4;
+    // The four waves' accumulators are exchanged in one pass, or in two (half of the
+    // head-dim tiles each) where one pass would not fit the LDS (five query tiles at head
+    // dim 128).
+    static constexpr int MRG1 = 4 * 64 * ACC * 4 + 2 * 4 * QR * 4;
+    static constexpr int PH = TAB + (RING > MRG1 ? RING : MRG1) + 2 * 16 * G::RB > 160 * 1024 ? 2 : 1;
+    static constexpr int MRG = 4 * 64 * (ACC / PH) * 4 + 2 * 4 * QR * 4;
     static constexpr int NEW = TAB + (RING > MRG ? RING : MRG);   // new-token rows: 16 K, 16 V
     static constexpr int LDS = NEW + 2 * 16 * G::RB;
     static_assert(LDS <= 160 * 1024, "LDS budget");
@@ -446,23 +451,20 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
         math(kop, vop, false, nsel, true, nsel + a.nv);
     }
 
-    // ---- merge the four waves in one LDS exchange: every wave publishes its maxima,
-    //      sums and O^T accumulators, then wave w merges head-dim tiles
-    //      [w*DVT/4, (w+1)*DVT/4) of every row and writes them ----
+    // ---- merge the four waves through LDS: every wave publishes its maxima, sums and
+    //      O^T accumulators (all head-dim tiles, or half of them per phase), then wave w
+    //      merges a quarter of the published tiles of every row and writes them ----
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         lrun[qt] += __shfl_xor(lrun[qt], 16);
         lrun[qt] += __shfl_xor(lrun[qt], 32);
     }
-    float *xAcc = reinterpret_cast<float *>(lds + S::TAB);   // [wave][dv tile][qt][lane][4]
-    float *xM = xAcc + 4 * 64 * S::ACC;                       // [wave][QR]
+    constexpr int DVTP = G::DVT / S::PH;   // head-dim tiles exchanged per phase
+    constexpr int DPW = DVTP / 4;          // head-dim tiles merged by each wave per phase
+    float *xAcc = reinterpret_cast<float *>(lds + S::TAB);   // [wave][dv tile of the phase][qt][lane][4]
+    float *xM = xAcc + 4 * 64 * (S::ACC / S::PH);             // [wave][QR]
     float *xL = xM + 4 * S::QR;
     __syncthreads();                  // every wave is done with its ring
-#pragma unroll
-    for (int i = 0; i < G::DVT; ++i)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-            *reinterpret_cast<f32x4 *>(xAcc + (((w * G::DVT + i) * QT + qt) * 64 + lane) * 4) = acc[i][qt];
     if (quad == 0) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
@@ -470,54 +472,62 @@ __global__ __launch_bounds__(kThreads) void verify_attn_split_kernel(AttnArgs a)
             xL[w * S::QR + qt * 16 + li] = lrun[qt];
         }
     }
-    __syncthreads();
-
-    constexpr int DPW = G::DVT / 4;   // head-dim tiles merged by each wave
     const int64_t pstride = (int64_t)S::QR * D + 2 * S::QR;
     float *part = a.part + ((int64_t)pair * a.splits + split) * pstride;
 #pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-        const int q = qt * 16 + li;
-        const int row = qg * S::QR + q;
-        if (row >= a.GV)
-            continue;                 // padding rows are never written
-        float mw[4], M = -INFINITY;
+    for (int ph = 0; ph < S::PH; ++ph) {
+        if (ph > 0)
+            __syncthreads();          // the previous phase's tiles have been read
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            mw[v] = xM[v * S::QR + q];
-            M = fmaxf(M, mw[v]);
-        }
-        float f[4], l = 0.f;
+        for (int i = 0; i < DVTP; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            f[v] = M == -INFINITY ? 0.f : fast_exp2(mw[v] - M);
-            l += f[v] * xL[v * S::QR + q];
-        }
-        const int t = row / a.G;
-        const int h = g * a.G + (row - t * a.G);
-        const float inv = 1.f / l;
+            for (int qt = 0; qt < QT; ++qt)
+                *reinterpret_cast<f32x4 *>(xAcc + (((w * DVTP + i) * QT + qt) * 64 + lane) * 4) = acc[ph * DVTP + i][qt];
+        __syncthreads();
 #pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-            const int i = w * DPW + j;
-            f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int qt = 0; qt < QT; ++qt) {
+            const int q = qt * 16 + li;
+            const int row = qg * S::QR + q;
+            if (row >= a.GV)
+                continue;             // padding rows are never written
+            float mw[4], M = -INFINITY;
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                o += f[v] * *reinterpret_cast<const f32x4 *>(xAcc + (((v * G::DVT + i) * QT + qt) * 64 + lane) * 4);
-            const int dv = i * 16 + 4 * quad;
-            if (a.splits == 1) {
-                uint16_t *op = a.out + ((int64_t)(b * a.nv + t) * a.Hq + h) * D + dv;
-                *reinterpret_cast<u32x2 *>(op) =
-                    u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
-            } else {
-                *reinterpret_cast<f32x4 *>(part + (int64_t)q * D + dv) = o;
+            for (int v = 0; v < 4; ++v) {
+                mw[v] = xM[v * S::QR + q];
+                M = fmaxf(M, mw[v]);
             }
-        }
-        if (w == 0 && quad == 0) {
-            if (a.splits == 1) {
-                a.lse[((int64_t)b * a.Hq + h) * a.nv + t] = (M + __log2f(l)) * kLn2;
-            } else {
-                part[S::QR * D + q] = M;
-                part[S::QR * D + S::QR + q] = l;
+            float f[4], l = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                f[v] = M == -INFINITY ? 0.f : fast_exp2(mw[v] - M);
+                l += f[v] * xL[v * S::QR + q];
+            }
+            const int t = row / a.G;
+            const int h = g * a.G + (row - t * a.G);
+            const float inv = 1.f / l;
+#pragma unroll
+            for (int j = 0; j < DPW; ++j) {
+                const int i = w * DPW + j;
+                f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    o += f[v] * *reinterpret_cast<const f32x4 *>(xAcc + (((v * DVTP + i) * QT + qt) * 64 + lane) * 4);
+                const int dv = (ph * DVTP + i) * 16 + 4 * quad;
+                if (a.splits == 1) {
+                    uint16_t *op = a.out + ((int64_t)(b * a.nv + t) * a.Hq + h) * D + dv;
+                    *reinterpret_cast<u32x2 *>(op) =
+                        u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
+                } else {
+                    *reinterpret_cast<f32x4 *>(part + (int64_t)q * D + dv) = o;
+                }
+            }
+            if (ph == 0 && w == 0 && quad == 0) {
+                if (a.splits == 1) {
+                    a.lse[((int64_t)b * a.Hq + h) * a.nv + t] = (M + __log2f(l)) * kLn2;
+                } else {
+                    part[S::QR * D + q] = M;
+                    part[S::QR * D + S::QR + q] = l;
+                }
             }
         }
     }
@@ -620,7 +630,8 @@ hipError_t launch_r(const AttnArgs &a, int qt, dim3 grid, hipStream_t st)
     case 1: return launch_qt<D, 1, R>(a, grid, st);
     case 2: return launch_qt<D, 2, R>(a, grid, st);
     case 3: return launch_qt<D, 3, R>(a, grid, st);
-    default: return launch_qt<D, 4, R>(a, grid, st);
+    case 4: return launch_qt<D, 4, R>(a, grid, st);
+    default: return launch_qt<D, 5, R>(a, grid, st);
     }
 }
 

@@ -10,7 +10,7 @@
 namespace dustin {
 
 // ---------------------------------------------------------------- attention
-constexpr int kMaxQT = 4;          // 16-row query tiles held by one workgroup
+constexpr int kMaxQT = 5;          // 16-row query tiles held by one workgroup
 constexpr int kSplitMax = 2048;    // selected positions of one workgroup (64 steps of 32) when K
                                    // and V rows share their offsets; half as many when they do not
 constexpr int kMaxSplits = 256;    // splits of one (sequence, KV head, query group)

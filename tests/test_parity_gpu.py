@@ -301,3 +301,14 @@ def test_scores_repeat_bitwise():
         else:
             assert torch.equal(got[0], first[0]) and torch.equal(got[1], first[1]), f"call {r} differs"
     say("  four scoring calls bitwise equal")
+
+
+def test_five_query_tiles():
+    """72 query rows per KV head (G = 8, gamma = 8) fill five 16-row tiles in one workgroup:
+    at head dim 128 the waves exchange their accumulators in two phases, at head dim 64 in
+    one; 144 rows (G = 16) run as two query groups of five tiles."""
+    for name, w in (("qt5_d128", small("qt5_d128", 2, 1100, 16, 2, 128, 8, 256, 4, 32, 64, seed=22)),
+                    ("qt5_d64", small("qt5_d64", 2, 1100, 16, 2, 64, 8, 256, 4, 32, 64, seed=23)),
+                    ("qt5x2_d128", small("qt5x2_d128", 2, 900, 32, 2, 128, 8, 200, 4, 16, 40, seed=24))):
+        say(f"[{name}]")
+        check_pipeline(W.make_inputs(w, device="cuda"), [0], [0], [0, 1])
