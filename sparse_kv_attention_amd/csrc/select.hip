@@ -77,7 +77,7 @@ struct SelShared {
 // Threshold of the `kth` largest eligible key (1 <= kth <= #eligible): returns the
 // threshold key and, in `need`, how many keys equal to it belong to the top kth.
 // Per 8-bit pass: every thread counts its keys into the current histogram (lane-slot
-// copies, one atomic per run of equal digits); barrier; every thread sums one bin over
+// copies, one atomic per counted key); barrier; every thread sums one bin over
 // a quarter of the copies and clears its share of the other histogram (for the next
 // pass); barrier; wave 0 adds the four quarters of its 4 bins per lane, scans the bins
 // from the top with shuffles and picks the digit; a last barrier publishes it.  hist[0]
@@ -97,27 +97,15 @@ __device__ uint32_t radix_select(const uint32_t (&key)[E], uint64_t elig, int kt
         const int shift = 24 - 8 * pass;
         uint32_t *hist = sh.hist[pass & 1];
         uint32_t *other = sh.hist[(pass + 1) & 1];
-        // The thread's keys are consecutive positions, and in the early passes most of them
-        // share a digit: runs of equal digits are counted in a register and added with one
-        // atomic per run (keys that do not take part leave the current run open).
-        int cur = -1;
-        uint32_t run = 0;
+        // every eligible key that agrees with the prefix found so far adds one to its
+        // digit's counter (a masked LDS atomic per key, no branches around it)
+        const uint32_t hmask = pass == 0 ? 0u : ~0u << (shift + 8);
+        const uint32_t want = prefix & hmask;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            const bool match = pass == 0 || (key[e] >> (shift + 8)) == (prefix >> (shift + 8));
-            if (((elig >> e) & 1) && match) {
-                const int d = (key[e] >> shift) & 255;
-                if (d != cur) {
-                    if (run)
-                        atomicAdd(&hist[slot * kHistStride + cur], run);
-                    cur = d;
-                    run = 0;
-                }
-                ++run;
-            }
+            if (((elig >> e) & 1) && (key[e] & hmask) == want)
+                atomicAdd(&hist[slot * kHistStride + ((key[e] >> shift) & 255)], 1u);
         }
-        if (run)
-            atomicAdd(&hist[slot * kHistStride + cur], run);
         __syncthreads();
         {
             constexpr int kQ = kSelectThreads / 256;          // quarters of the copies
@@ -259,16 +247,11 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
     const int md = a.score_draft ? clampi(m_raw, 0, k - s - w) : 0;
     const int r = k - s - w - md;
 
-    uint64_t valid = 0, prot = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int t = base + e;
-        if (t < N) {
-            valid |= 1ull << e;
-            if (t < s || t >= N - w)
-                prot |= 1ull << e;
-        }
-    }
+    // the thread's positions base + e: valid below N, protected below s (sinks) or at N - w
+    // and above (window); masks of the lowest n bits, n in [0, E]
+    auto low = [](int n) -> uint64_t { return n >= 64 ? ~0ull : (1ull << n) - 1; };
+    const uint64_t valid = low(clampi(N - base, 0, E));
+    const uint64_t prot = low(clampi(s - base, 0, E)) | (valid & ~low(clampi(N - w - base, 0, E)));
     for (int i = tid; i < kCopies * kHistStride; i += kSelectThreads)
         sh.hist[0][i] = 0;
     __syncthreads();
@@ -285,6 +268,25 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
     const uint64_t fin = prot | selD | selT;
     int total;
     int o = block_scan(__popcll(fin), total, sh.scan);
+    constexpr int kStageWords = 2 * kCopies * kHistStride;
+    if (a.k_max <= kStageWords) {
+        // the histograms are no longer needed: the positions are placed there in order and
+        // then written out with coalesced stores
+        int32_t *stage = reinterpret_cast<int32_t *>(&sh.hist[0][0]);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (((fin >> e) & 1) && o < a.k_max)
+                stage[o++] = base + e;
+        __syncthreads();
+        const int n_out = min(total, a.k_max);
+        for (int i = tid; i < a.k_max; i += kSelectThreads) {
+            if (i >= k)
+                out[i] = -1;
+            else if (i < n_out)
+                out[i] = stage[i];
+        }
+        return;
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e)
         if (((fin >> e) & 1) && o < a.k_max)
