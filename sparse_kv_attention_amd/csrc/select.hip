@@ -71,27 +71,31 @@ struct SelShared {
     uint32_t hist[2][kCopies * kHistStride];   // alternating: one is counted, the other cleared
     int part[kSelectThreads / 256][256];       // per-bin sums over a quarter of the copies
     int scan[kWaves + 1];
-    int bcast[2];
+    int bcast[3];
 };
 
 // Threshold of the `kth` largest eligible key (1 <= kth <= #eligible): returns the
-// threshold key and, in `need`, how many keys equal to it belong to the top kth.
+// threshold key and, in `need`, how many keys equal to it belong to the top kth.  When,
+// before the last pass, every key of the digit bin just chosen belongs to the top kth, the
+// search stops there: `whole` is set, and the top kth are exactly the keys >= the returned
+// prefix (its lower digits zero).
 // Per 8-bit pass: every thread counts its keys into the current histogram (lane-slot
 // copies, one atomic per counted key); barrier; every thread sums one bin over
 // a quarter of the copies and clears its share of the other histogram (for the next
 // pass); barrier; wave 0 adds the four quarters of its 4 bins per lane, scans the bins
 // from the top with shuffles and picks the digit; a last barrier publishes it.  hist[0]
-// must be zero on entry and is zero again on return (the last pass counts into hist[1],
-// which the next call's first pass clears).
+// must be zero on entry and is zero again on return (an odd pass counts into hist[1],
+// which the next call's first pass clears; a stop after an even pass clears hist[0]).
 template <int E>
 __device__ uint32_t radix_select(const uint32_t (&key)[E], uint64_t elig, int kth, int &need,
-                                 SelShared &sh)
+                                 bool &whole, SelShared &sh)
 {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int slot = lane % kCopies;
     uint32_t prefix = 0;
     need = kth;
+    whole = false;
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
@@ -146,6 +150,7 @@ __device__ uint32_t radix_select(const uint32_t (&key)[E], uint64_t elig, int kt
                 if (before < need && before + c[j] >= need) {
                     sh.bcast[0] = 255 - 4 * lane - j;
                     sh.bcast[1] = need - before;
+                    sh.bcast[2] = c[j];
                 }
                 before += c[j];
             }
@@ -153,6 +158,15 @@ __device__ uint32_t radix_select(const uint32_t (&key)[E], uint64_t elig, int kt
         __syncthreads();
         prefix |= (uint32_t)sh.bcast[0] << shift;
         need = sh.bcast[1];
+        if (pass < 3 && need == sh.bcast[2]) {   // the whole bin is taken (uniform)
+            whole = true;
+            if ((pass & 1) == 0) {
+                for (int i = tid; i < kCopies * kHistStride; i += kSelectThreads)
+                    hist[i] = 0;
+                __syncthreads();
+            }
+            break;
+        }
     }
     return prefix;
 }
@@ -162,8 +176,15 @@ template <int E>
 __device__ uint64_t take_top(const uint32_t (&key)[E], uint64_t elig, int kth, SelShared &sh)
 {
     int need;
-    const uint32_t thr = radix_select<E>(key, elig, kth, need, sh);
+    bool whole;
+    const uint32_t thr = radix_select<E>(key, elig, kth, need, whole, sh);
     uint64_t sel = 0;
+    if (whole) {
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            sel |= (uint64_t)(((elig >> e) & 1) && key[e] >= thr) << e;
+        return sel;
+    }
     int eq = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {   // branch-free

@@ -312,3 +312,51 @@ def test_five_query_tiles():
                     ("qt5x2_d128", small("qt5x2_d128", 2, 900, 32, 2, 128, 8, 200, 4, 16, 40, seed=24))):
         say(f"[{name}]")
         check_pipeline(W.make_inputs(w, device="cuda"), [0], [0], [0, 1])
+
+
+def test_selection_stops_early_on_a_whole_digit_bin():
+    """Planted scores make the radix search stop before its last pass because every key of
+    the chosen digit bin belongs to the top set: after the first pass (draft tier of
+    sequence 0), after the second (sequence 1), after the third in both tiers (sequence 2);
+    all-equal scores (sequence 3) run every pass and take ties by position.  The target
+    tier after an early draft stop must see clean histograms.  Bit-exact against the
+    oracle on the same fp32 scores, 32k context (32 keys per thread), budget 512."""
+    from sparse_kv_attention_amd import dustin as D
+    B, n_max, k_max = 4, 32768, 512
+    ctx = np.array([32768, 30000, 32768, 20000], dtype=np.int32)
+    s, wdw, m = 4, 64, 256
+    r = k_max - s - wdw - m                      # 188 target picks
+    gen = np.random.default_rng(31)
+    sd = gen.uniform(1e-6, 1e-3, (B, n_max)).astype(np.float32)
+    st = gen.uniform(1e-6, 1e-3, (B, n_max)).astype(np.float32)
+    u = lambda bits: np.asarray(bits, dtype=np.uint32).view(np.float32)
+    pos = lambda b, n: gen.choice(np.arange(s, ctx[b] - wdw), n, replace=False)
+    # sequence 0: the m draft keys alone above 1.0 (one top-byte bin)
+    sd[0, pos(0, m)] = u(0x3F800000 + 4096 * np.arange(m))
+    # sequence 1: m draft keys 0.75 + i*2^-16 share two bytes; 5 keys at 0.5 share the first
+    p1 = pos(1, m + 5)
+    sd[1, p1[:m]] = u(0x3F400000 + 256 * np.arange(m))
+    sd[1, p1[m:]] = u(0x3F000000 + np.arange(5))
+    # sequence 2: in both tiers the picks share three bytes, 3 keys share only two (the
+    # target keys at positions the draft tier does not take)
+    p2 = pos(2, m + r + 6)
+    for sc, pp, n in ((sd, p2[:m + 3], m), (st, p2[m + 3:], r)):
+        sc[2, pp[:n]] = u(0x3F400400 + np.arange(n))
+        sc[2, pp[n:]] = u(0x3F400000 + np.arange(3))
+    sd[3] = 0.0
+    st[3] = 0.0
+    dev = "cuda"
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    full = lambda v: torch.full((B,), v, dtype=torch.int32, device=dev)
+    idx = torch.full((B, k_max), -5, dtype=torch.int32, device=dev)
+    cnt = torch.zeros((B,), dtype=torch.int32, device=dev)
+    ws = D.workspace(D.dustin_select_workspace_size(B, n_max), dev)
+    for rep in range(2):
+        D.dustin_select(t(ctx), t(sd), t(st), full(k_max), full(s), full(wdw), full(m), idx, cnt, ws)
+        torch.cuda.synchronize()
+        want_idx, want_cnt = O.select(ctx, sd, st, [k_max] * B, [s] * B, [wdw] * B, [m] * B, k_max)
+        assert np.array_equal(cnt.cpu().numpy(), want_cnt)
+        got = idx.cpu().numpy()
+        for b in range(B):
+            assert np.array_equal(got[b], want_idx[b]), f"sequence {b} call {rep}"
+    say("  early stops after passes 1, 2, 3 and the all-ties case bit-exact")
