@@ -360,3 +360,13 @@ def test_selection_stops_early_on_a_whole_digit_bin():
         for b in range(B):
             assert np.array_equal(got[b], want_idx[b]), f"sequence {b} call {rep}"
     say("  early stops after passes 1, 2, 3 and the all-ties case bit-exact")
+
+
+def test_context_above_32k():
+    """Contexts of 30k..50k tokens (ragged): 64 keys per selection thread (the widest
+    selection variant), scoring over 50k-token rows, a 4096-token budget over two splits
+    and more; every stage against the oracle."""
+    w = W.shrink(small("long_ctx", 3, 50000, 8, 2, 128, 4, 4096, 4, 64, 1024, seed=25), ragged_lo=30000)
+    inp = W.make_inputs(w, device="cuda")
+    assert inp.n_max > 32768
+    check_pipeline(inp, [0], [], [0, 1, 2])
