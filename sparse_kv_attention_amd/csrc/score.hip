@@ -606,8 +606,8 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
 
 constexpr int kFinTokens = 1024;          // = kThreads * 4: every thread sums four tokens
 constexpr int kFinTiles = kFinTokens / kStatTile;
-constexpr int kFinBatch = 8;
-constexpr int kFinChunk = 32;              // pairs whose logits one finalize thread holds at once               // pairs per wave whose loads are in flight together
+constexpr int kFinBatch = 8;               // pairs per wave whose statistics loads are in flight together
+constexpr int kFinChunk = 32;              // pairs whose logits one finalize thread holds at once
 
 __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
 {
