@@ -370,3 +370,49 @@ def test_context_above_32k():
     inp = W.make_inputs(w, device="cuda")
     assert inp.n_max > 32768
     check_pipeline(inp, [0], [], [0, 1, 2])
+
+
+def test_selection_parameter_edges():
+    """Per-sequence parameters at their edges, through the C ABI against the oracle:
+    empty and 1-token contexts, budgets of 0 and above k_max, sinks alone exceeding the
+    budget, sinks + window exceeding it, m above what is left and m = 0, on scores with
+    many ties (quantised), -0/+0 and negative values; 5000 positions (5 keys per thread,
+    the scalar-load path at a length that is not a multiple of 4)."""
+    from sparse_kv_attention_amd import dustin as D
+    B, n_max, k_max = 10, 4999, 700
+    ctx = np.array([0, 1, 4999, 3000, 2500, 4000, 700, 701, 4999, 1234], dtype=np.int32)
+    budget = np.array([5, 5, 0, 10000, 64, 300, 700, 700, 512, 200], dtype=np.int32)
+    sink = np.array([2, 4, 3, 16, 100, 8, 0, 700, 4, 0], dtype=np.int32)
+    window = np.array([1, 4, 3, 64, 10, 400, 0, 1, 32, 0], dtype=np.int32)
+    m = np.array([1, 1, 5, 100, 5, 50, 350, 3, 10000, 0], dtype=np.int32)
+    gen = np.random.default_rng(41)
+    sd = np.round(gen.normal(0, 1, (B, n_max)) * 4) / 4           # few distinct values: ties
+    st = np.round(gen.normal(0, 1, (B, n_max)) * 16) / 16
+    sd[4, ::7] = -0.0
+    sd[4, 1::7] = 0.0
+    st[9] = 0.0
+    sd, st = sd.astype(np.float32), st.astype(np.float32)
+    dev = "cuda"
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    idx = torch.full((B, k_max), -5, dtype=torch.int32, device=dev)
+    cnt = torch.zeros((B,), dtype=torch.int32, device=dev)
+    ws = D.workspace(D.dustin_select_workspace_size(B, n_max), dev)
+    for draft in (sd, None):
+        D.dustin_select(t(ctx), None if draft is None else t(draft), t(st), t(budget), t(sink), t(window),
+                        t(m), idx, cnt, ws)
+        torch.cuda.synchronize()
+        want_idx, want_cnt = O.select(ctx, draft, st, budget, sink, window, m, k_max)
+        assert np.array_equal(cnt.cpu().numpy(), want_cnt), (cnt.cpu().numpy(), want_cnt)
+        got = idx.cpu().numpy()
+        for b in range(B):
+            assert np.array_equal(got[b], want_idx[b]), f"sequence {b}, draft tier {draft is not None}"
+    say(f"  counts {want_cnt.tolist()} bit-exact, with and without the draft tier")
+
+
+def test_one_query_head_per_kv_head():
+    """Multi-head attention (G = 1): five verify rows per KV head, one query tile with
+    eleven padding rows; head dim 128 and 64."""
+    for name, w in (("mha_d128", small("mha_d128", 3, 900, 4, 4, 128, 4, 200, 4, 16, 40, seed=26)),
+                    ("mha_d64", small("mha_d64", 2, 700, 6, 6, 64, 2, 150, 2, 8, 30, seed=27))):
+        say(f"[{name}]")
+        check_pipeline(W.make_inputs(w, device="cuda"), [0], [0], [0, 1])
