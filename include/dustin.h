@@ -110,6 +110,7 @@ const char *dustin_status_string(dustin_status s);
  * committed context [0, ctx_len[b]).
  *   groups : (host) [n_groups], 1 <= n_groups <= 16; all groups share head_dim
  *   q      : bf16 [B][sum of n_qheads][n_q][head_dim], heads in group order
+ *   scale  : any finite value (0 and negative included); non-finite -> INVALID_ARG
  *   head_dim in {64, 128}; 1 <= n_q <= 16; pairs per group (n_qheads * queries used)
  *   at most 16 in PROB_SUM mode and 64 in the logit-sum modes
  *   score  : fp32 [B][n_max], fully written
@@ -156,6 +157,7 @@ dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const floa
  *   out[b][t][h] = sum_x softmax_x(scale * q[b][t][h] . K[b][x][g]) V[b][x][g]
  *   lse[b][h][t] = ln sum_x exp(scale * q[b][t][h] . K[b][x][g])
  *   q, out : bf16 [B][n_verify][Hq][head_dim];  lse : fp32 [B][Hq][n_verify]
+ *   scale  : any finite value (0 and negative included); non-finite -> INVALID_ARG
  *   head_dim in {64, 128}; 1 <= n_verify <= 16; Hq % Hkv == 0;
  *   k_max + n_verify (dense: n_max + n_verify) <= 131072
  *   workspace: dustin_sparse_verify_attn_workspace_size(...) bytes, any contents (it

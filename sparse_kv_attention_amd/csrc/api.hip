@@ -3,6 +3,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <cmath>
 
 #include "dustin.h"
 #include "kv.hpp"
@@ -140,7 +141,7 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
         return DUSTIN_ERR_INVALID_ARG;
     if (sparse && (!idx || !count || k_max < 0))
         return DUSTIN_ERR_INVALID_ARG;
-    if (n_max < 0 || !(scale == scale))
+    if (n_max < 0 || !std::isfinite(scale))
         return DUSTIN_ERR_INVALID_ARG;
     if (!view_ok(k, Hkv, n_verify) || !view_ok(v, Hkv, n_verify))
         return DUSTIN_ERR_INVALID_ARG;
@@ -251,7 +252,7 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
                                float scale, int mode, float *score, void *workspace,
                                size_t workspace_bytes, void *stream)
 {
-    if (B < 0 || n_max < 0 || n_q <= 0 || !(scale == scale))
+    if (B < 0 || n_max < 0 || n_q <= 0 || !std::isfinite(scale))
         return DUSTIN_ERR_INVALID_ARG;
     if (!score_mode_ok(mode))
         return DUSTIN_ERR_INVALID_ARG;

@@ -40,8 +40,9 @@ def signal_spec(inp: Inputs, signal: str):
     return inp.target_groups, inp.q_srh_target, inp.k_cache, 1.0 / math.sqrt(w.target.d)
 
 
-def oracle_scores(inp: Inputs, signal: str, mode: int, bsel):
-    groups, q, caches, scale = signal_spec(inp, signal)
+def oracle_scores(inp: Inputs, signal: str, mode: int, bsel, scale=None):
+    groups, q, caches, default_scale = signal_spec(inp, signal)
+    scale = default_scale if scale is None else scale
     ctx = inp.ctx_len.cpu().numpy()[bsel]
     acc = np.zeros((len(bsel), inp.n_max), dtype=np.float64)
     qoff = 0
@@ -90,14 +91,14 @@ def oracle_select_on(inp: Inputs, sd: np.ndarray, st: np.ndarray, bsel, pure_top
     return O.select(c(inp.ctx_len), sd, st, c(inp.budget), c(inp.n_sink), c(inp.n_window), c(inp.m), inp.k_max)
 
 
-def oracle_attn(inp: Inputs, layer: int, idx, count, bsel, dense=False):
+def oracle_attn(inp: Inputs, layer: int, idx, count, bsel, dense=False, scale=None):
     """Returns (O float64 [len(bsel)][nv][Hq][d], lse [len(bsel)][Hq][nv])."""
     ctx = inp.ctx_len.cpu().numpy()
     n_rows = int(max(ctx[b] for b in bsel)) + inp.w.n_verify
     K = np.stack([u16(rows(inp, inp.k_cache[layer], b, n_rows)) for b in bsel])
     V = np.stack([u16(rows(inp, inp.v_cache[layer], b, n_rows)) for b in bsel])
     Q = u16(inp.q_verify[layer][bsel])
-    scale = 1.0 / math.sqrt(inp.w.target.d)
+    scale = 1.0 / math.sqrt(inp.w.target.d) if scale is None else scale
     if dense:
         return O.verify_attn(Q, K, V, ctx[bsel], None, None, scale, inp.w.target.hkv)
     return O.verify_attn(Q, K, V, ctx[bsel], idx[bsel], count[bsel], scale, inp.w.target.hkv)

@@ -70,6 +70,8 @@ def sparse(**kw):
     (dict(cnt=None), D.ERR_INVALID_ARG),
     (dict(k_max=-1), D.ERR_INVALID_ARG),
     (dict(scale=float("nan")), D.ERR_INVALID_ARG),
+    (dict(scale=float("inf")), D.ERR_INVALID_ARG),
+    (dict(scale=float("-inf")), D.ERR_INVALID_ARG),
     (dict(k=view(base=None)), D.ERR_INVALID_ARG),
     (dict(k=view(stride_token=1001)), D.ERR_INVALID_ARG),
     (dict(v=view(n_heads=4)), D.ERR_INVALID_ARG),
@@ -117,13 +119,16 @@ def test_score_rejects():
         g[i].kv_head = i
         g[i].n_qheads = 1
     f = lambda **kw: D._score(2, kw.get("n_max", 4096), kw.get("ctx", FAKE), kw.get("ng", 2), kw.get("g", g),
-                              kw.get("d", 128), kw.get("q", FAKE), kw.get("nq", 5), 0.1, kw.get("mode", 0),
+                              kw.get("d", 128), kw.get("q", FAKE), kw.get("nq", 5), kw.get("scale", 0.1),
+                              kw.get("mode", 0),
                               kw.get("score", FAKE), kw.get("ws", FAKE), kw.get("wsb", 1 << 30), None)
     assert f(d=32) == D.ERR_UNSUPPORTED
     assert f(ng=17) == D.ERR_UNSUPPORTED
     assert f(nq=17) == D.ERR_UNSUPPORTED
     assert f(ng=0) == D.ERR_INVALID_ARG
     assert f(mode=5) == D.ERR_INVALID_ARG
+    for bad_scale in (float("nan"), float("inf"), float("-inf")):
+        assert f(scale=bad_scale) == D.ERR_INVALID_ARG
     assert f(q=None) == D.ERR_INVALID_ARG
     assert f(score=None) == D.ERR_INVALID_ARG
     assert f(ws=None) == D.ERR_WORKSPACE

@@ -416,3 +416,36 @@ def test_one_query_head_per_kv_head():
                     ("mha_d64", small("mha_d64", 2, 700, 6, 6, 64, 2, 150, 2, 8, 30, seed=27))):
         say(f"[{name}]")
         check_pipeline(W.make_inputs(w, device="cuda"), [0], [0], [0, 1])
+
+
+def test_negative_and_zero_scales():
+    """Any finite softmax scale: a negative one (the attention kernels move the sign into
+    Q; the scoring kernels multiply it in fp64) and zero (uniform softmax: every token
+    scores its pair count / N, so selection falls back to position order, and O is the
+    mean of the attended V rows), scoring, selection, sparse and dense attention against
+    the oracle."""
+    w = small("scales", 2, 900, 8, 2, 128, 4, 200, 4, 16, 40, seed=28)
+    inp = W.make_inputs(w, device="cuda")
+    for sc in (-0.09, 0.0):
+        say(f"[scale {sc}]")
+        step = step_for(inp, [0])
+        step.scale = sc
+        step.scale_draft = sc
+        step.score()
+        torch.cuda.synchronize()
+        sd = step.score_draft.cpu().numpy()
+        st = step.score_target.cpu().numpy()
+        check_scores(sd, oracle_scores(inp, "draft", O.PROB_SUM, [0, 1], scale=sc), "draft scores")
+        check_scores(st, oracle_scores(inp, "target", O.PROB_SUM, [0, 1], scale=sc), "target scores")
+        step.select()
+        torch.cuda.synchronize()
+        idx_o, cnt_o = oracle_select_on(inp, sd.astype(np.float64), st.astype(np.float64), [0, 1])
+        idx_g, cnt_g = step.idx.cpu().numpy(), step.count.cpu().numpy()
+        assert np.array_equal(cnt_g, cnt_o) and np.array_equal(idx_g[:, :inp.k_max], idx_o)
+        step.attn(0)
+        torch.cuda.synchronize()
+        check_attn(step.out, step.lse, oracle_attn(inp, 0, idx_g, cnt_g, [0, 1], scale=sc), [0, 1], "sparse")
+        step.dense(0)
+        torch.cuda.synchronize()
+        check_attn(step.out, step.lse, oracle_attn(inp, 0, None, None, [0, 1], dense=True, scale=sc), [0, 1],
+                   "dense")
