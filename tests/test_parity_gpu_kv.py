@@ -17,7 +17,7 @@ from oracle import oracle as O
 from sparse_kv_attention_amd import dustin as D
 from sparse_kv_attention_amd import workloads as W
 from sparse_kv_attention_amd.pipeline import SparseVerifyStep
-from test_parity_gpu import small
+from test_parity_gpu import check_pipeline, small
 
 pytestmark = pytest.mark.gpu
 
@@ -281,3 +281,17 @@ def test_vegas_aggregate_over_every_head_of_a_layer(all_queries):
                             inp.k_max)
     assert np.array_equal(step.count.cpu().numpy(), cnt_o)
     assert np.array_equal(step.idx.cpu().numpy()[:, :inp.k_max], idx_o)
+
+
+def test_page_size_one():
+    """Pages of one token (the page-size-1 layout of the Vegas summary's PagedAttention
+    change): every row is reached through its own page-table entry.  Scoring, selection,
+    sparse and dense attention against the oracle, then the verified block written through
+    the one-token pages."""
+    w = W.shrink(W.RAGGED_PAGED, batch=3, n_ctx=2500, ragged_lo=600, page_size=1,
+                 target=W.ModelShape(1, 64, 8, 128), srh_target=((0, 0), (0, 8)))
+    inp = W.make_inputs(w, device="cuda")
+    assert inp.paged and w.page_size == 1
+    ctx = inp.ctx_len.cpu().numpy()
+    check_pipeline(inp, [0], [0], b_attn=[int(np.argmin(ctx)), int(np.argmax(ctx))], b_dense=[int(np.argmin(ctx))])
+    check_write(inp, w.n_verify, seed=5)
