@@ -58,5 +58,24 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi_example.c")
+EXAMPLE_BIN = os.path.join(ROOT, "tests", "c_abi_example")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_example(verbose: bool = False) -> str:
+    """The C program under tests/ that calls libdustin.so through dustin.h alone (plain C,
+    the HIP runtime for device memory); found next to the library through its rpath."""
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(ROCM, "include"), EXAMPLE_SRC, "-o", EXAMPLE_BIN,
+           "-L", PKG, "-ldustin", "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/../sparse_kv_attention_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    return EXAMPLE_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_example(verbose=True))
