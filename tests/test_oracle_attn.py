@@ -7,6 +7,7 @@ import json
 import os
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import oracle as O
@@ -41,7 +42,10 @@ def test_worked_example():
         assert abs(lse[0, 0, 0] - c["expect_lse"]) < 1e-15
 
 
-def test_matches_torch_sdpa_float64():
+@pytest.mark.parametrize("scale", [0.3, -0.3, 0.0])
+def test_matches_torch_sdpa_float64(scale):
+    """Any finite scale, negative and zero included; at zero every attended row has the
+    same weight, so O is the plain mean of the attended V rows and LSE = ln(count)."""
     rng = np.random.default_rng(0)
     B, N, Hq, Hkv, d, nv = 2, 40, 6, 2, 16, 3
     n_cap = N + nv
@@ -52,7 +56,6 @@ def test_matches_torch_sdpa_float64():
     cnt = np.array([12, 7], np.int32)
     for b in range(B):
         idx[b, :cnt[b]] = np.sort(rng.choice(ctx[b], cnt[b], replace=False))
-    scale = 0.3
     Ov, lse = O.verify_attn(bits(Q), bits(K), bits(V), ctx, idx, cnt, scale, Hkv)
     G = Hq // Hkv
     for b in range(B):
@@ -71,6 +74,10 @@ def test_matches_torch_sdpa_float64():
             lg = (q @ k.T) * scale
             lg[~mask] = -np.inf
             np.testing.assert_allclose(lse[b, h], torch.logsumexp(lg, -1).numpy(), rtol=1e-13)
+            if scale == 0.0:
+                for t in range(nv):
+                    np.testing.assert_allclose(Ov[b, t, h], v[mask[t]].mean(0).numpy(), rtol=1e-12, atol=1e-13)
+                    assert abs(lse[b, h, t] - np.log(int(mask[t].sum()))) < 1e-13
 
 
 def test_full_budget_equals_dense():

@@ -7,6 +7,7 @@ German Vegas summary 2A/2B: raw logits summed over heads and the first/bonus que
 import itertools
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import oracle as O
@@ -26,13 +27,18 @@ def rand_stream(rng, B, n, d, nh, nq, scale=1.0):
     return K, Q
 
 
-def test_matches_torch_softmax_float64():
+@pytest.mark.parametrize("scale", [0.25, -0.25, 0.0])
+def test_matches_torch_softmax_float64(scale):
+    """Any finite scale, negative and zero included; at zero every pair's softmax is
+    uniform, so each token scores (pairs) / N."""
     rng = np.random.default_rng(0)
     B, n, d, nh, nq = 2, 37, 16, 3, 4
     K, Q = rand_stream(rng, B, n, d, nh, nq)
     ctx = np.array([37, 20])
-    scale = 0.25
     acc = O.score_stream(bits(K), bits(Q), ctx, n, scale, O.PROB_SUM)
+    if scale == 0.0:
+        for b in range(B):
+            np.testing.assert_allclose(acc[b, :ctx[b]], nh * nq / ctx[b], rtol=1e-13)
     for b in range(B):
         nb = ctx[b]
         lg = torch.einsum("hqd,nd->hqn", Q[b].double(), K[b, :nb].double()) * scale
