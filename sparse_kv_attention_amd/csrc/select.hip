@@ -5,12 +5,15 @@
 //
 // One workgroup of 1024 threads per sequence.  Thread t owns the contiguous positions
 // [t*E, t*E + E) and keeps their order-preserving 32-bit keys in registers.  Each tier
-// finds its threshold key with a 4-pass 8-bit LDS radix select (histograms are kept
-// per lane slot, with a padded stride, so lanes of one wave never contend for a counter
-// or a bank), takes every eligible key above the threshold plus the first `need` keys
-// equal to it in position order (block-wide exclusive scan), and the final set is
-// compacted in ascending position order with one more block scan.  Integer-only after
-// the key transform, so the result is bit-reproducible.
+// finds its threshold key with an LDS radix select of up to four 8-bit passes (32
+// histogram copies indexed by lane mod 32, with a padded stride: at most two lanes of a
+// wave share a counter, and lanes counting the same digit hit different banks).  It
+// takes every eligible key above the threshold plus the first `need` keys equal to it in
+// position order (block-wide exclusive scan); when every key of the chosen digit bin is
+// needed, the search stops there and takes the keys at or above that prefix.  The final
+// set is compacted in ascending position order with one more block scan, staged in LDS
+// and written with coalesced stores.  Integer-only after the key transform, so the
+// result is bit-reproducible.
 #include "device.hpp"
 #include "launch.hpp"
 
