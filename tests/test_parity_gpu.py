@@ -449,3 +449,13 @@ def test_negative_and_zero_scales():
         torch.cuda.synchronize()
         check_attn(step.out, step.lse, oracle_attn(inp, 0, None, None, [0, 1], dense=True, scale=sc), [0, 1],
                    "dense")
+
+
+def test_single_query_signals():
+    """gamma = 1: each draft group scores one (head, query) pair, the narrowest softmax
+    variant; gamma = 0 with the Collect-2 signal: one verify query, which the logit sum
+    counts once (first and bonus query coincide)."""
+    w = small("gamma1", 2, 800, 8, 2, 128, 1, 150, 2, 8, 30, seed=29)
+    check_pipeline(W.make_inputs(w, device="cuda"), [0], [], [0, 1])
+    w = small("collect2_nq1", 2, 900, 8, 2, 128, 0, 120, 0, 0, 0, seed=30)
+    check_pipeline(W.make_inputs(w, device="cuda"), [0], [], [0, 1], logit_sum2=True)
