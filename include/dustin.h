@@ -29,6 +29,13 @@
  *     values are defined by that clamping, not by the method.
  *   - The library keeps no state between calls.  Calls that share a workspace must be
  *     ordered on one stream.
+ *   - Two environment variables tune the attention calls (for experiments and tests; a
+ *     value that is not a positive integer is ignored):
+ *       DUSTIN_ATTN_TARGET_WGS  workgroups per round of the attention grid (default: the
+ *                               device's compute units).  It changes the split plan, so
+ *                               the workspace size and the order of the partial sums;
+ *                               a workspace sized under another value is rejected.
+ *       DUSTIN_ATTN_RING        LDS ring slots per wave at head dim 64: 3 (default) or 2.
  */
 #ifndef DUSTIN_H
 #define DUSTIN_H
