@@ -34,8 +34,10 @@
  *       DUSTIN_ATTN_TARGET_WGS  workgroups per round of the attention grid (default: the
  *                               device's compute units).  It changes the split plan, so
  *                               the workspace size and the order of the partial sums;
- *                               a workspace sized under another value is rejected.
- *       DUSTIN_ATTN_RING        LDS ring slots per wave at head dim 64: 3 (default) or 2.
+ *                               set it before the size queries (a workspace smaller than
+ *                               the plan needs is rejected with DUSTIN_ERR_WORKSPACE).
+ *       DUSTIN_ATTN_RING        LDS ring slots per wave at head dim 64: 3 (the default,
+ *                               and any value above) or 2 (values 1 and 2).
  */
 #ifndef DUSTIN_H
 #define DUSTIN_H
