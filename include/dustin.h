@@ -29,15 +29,17 @@
  *     values are defined by that clamping, not by the method.
  *   - The library keeps no state between calls.  Calls that share a workspace must be
  *     ordered on one stream.
- *   - Two environment variables tune the attention calls (for experiments and tests; a
- *     value that is not a positive integer is ignored):
- *       DUSTIN_ATTN_TARGET_WGS  workgroups per round of the attention grid (default: the
- *                               device's compute units).  It changes the split plan, so
+ *   - Two environment variables tune the attention calls (for experiments and tests;
+ *     values other than those listed are ignored):
+ *       DUSTIN_ATTN_TARGET_WGS  a positive integer: workgroups per round of the attention
+ *                               grid (default: the device's compute units).  It changes the split plan, so
  *                               the workspace size and the order of the partial sums;
  *                               set it before the size queries (a workspace smaller than
  *                               the plan needs is rejected with DUSTIN_ERR_WORKSPACE).
- *       DUSTIN_ATTN_RING        LDS ring slots per wave at head dim 64: 3 (the default,
- *                               and any value above) or 2 (values 1 and 2).
+ *       DUSTIN_ATTN_FUSED_MERGE "1": the budget splits of one (sequence, KV head) are
+ *                               combined by the workgroup that finishes last, in the
+ *                               attention kernel itself; "0" (the default): by a second
+ *                               kernel.  Both give bit-identical results.
  */
 #ifndef DUSTIN_H
 #define DUSTIN_H
@@ -169,8 +171,13 @@ dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const floa
  *   scale  : any finite value (0 and negative included); non-finite -> INVALID_ARG
  *   head_dim in {64, 128}; 1 <= n_verify <= 16; Hq % Hkv == 0;
  *   k_max + n_verify (dense: n_max + n_verify) <= 131072
- *   workspace: dustin_sparse_verify_attn_workspace_size(...) bytes, any contents (it
- *   holds the partial results of the budget splits between the two kernels of a call).
+ *   workspace: dustin_sparse_verify_attn_workspace_size(...) bytes, 16-byte aligned, any
+ *   contents on the first call (it holds the partial results of the budget splits and
+ *   one arrival counter per (sequence, KV head, query group); a counter is recognised
+ *   by a 40-bit tag and left cleared by the call that used it).
+ *   Paged views (and contiguous views next to a paged one): every page and batch stride
+ *   must be a multiple of stride_token and the rows addressed below 2^32 rows, else
+ *   DUSTIN_ERR_UNSUPPORTED.
  * dense_verify_attn is the same with I_b = [0, ctx_len[b]); n_max bounds ctx_len.
  * ------------------------------------------------------------------------------- */
 dustin_status dustin_sparse_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_dim,

@@ -53,6 +53,20 @@ int env_int(const char *name, int dflt)
     return v > 0 ? v : dflt;
 }
 
+// A 0/1 switch from the environment ("0" turns it off; unset or anything else keeps dflt
+// unless it is "1").
+bool env_flag(const char *name, bool dflt)
+{
+    const char *s = getenv(name);
+    if (!s || !*s)
+        return dflt;
+    if (s[0] == '0' && s[1] == 0)
+        return false;
+    if (s[0] == '1' && s[1] == 0)
+        return true;
+    return dflt;
+}
+
 // Compute units of the current device (cached per device id).
 int device_cus()
 {
@@ -70,8 +84,8 @@ int device_cus()
 }
 
 // Workgroups per round of the attention grid: one resident workgroup per CU (the
-// per-wave tile rings take most of the LDS).  The split count is rounded so the grid is
-// a whole number of rounds.
+// per-wave rings take most of the LDS).  The split count is rounded so the grid is a
+// whole number of rounds.
 int attn_target_wgs()
 {
     return env_int("DUSTIN_ATTN_TARGET_WGS", device_cus());
@@ -79,34 +93,52 @@ int attn_target_wgs()
 
 struct AttnWs {
     AttnPlan plan;
-    size_t part_off, bytes;
+    size_t ctr_off, part_off, bytes;
 };
 
-// Positions one attention workgroup can hold: its LDS offset table is shared by K and V
-// when their rows sit at the same offsets, else halved between them.
-int attn_split_cap(bool kv_same) { return kv_same ? kSplitMax : 1024; }
+// Positions one attention workgroup can hold.  Sparse lists and paged caches take their
+// rows from each wave's LDS table (K and V rows sharing one table when they sit at the
+// same places, else half each); dense unpaged calls compute rows from positions and
+// take any length.
+int attn_split_cap(bool table, bool two_tables)
+{
+    return !table ? kMaxList : (two_tables ? kSplitMax / 2 : kSplitMax);
+}
 
-AttnWs attn_workspace(int B, int Hq, int Hkv, int n_verify, int max_list, bool kv_same)
+AttnWs attn_workspace(int B, int Hq, int Hkv, int head_dim, int n_verify, int max_list, int split_cap)
 {
     AttnWs w;
     const int G = Hq / Hkv;
-    w.plan = plan_attn(B, Hkv, G, n_verify, max_list, attn_target_wgs(), attn_split_cap(kv_same));
-    w.part_off = 0;
-    w.bytes = align_up(sizeof(float) * w.plan.part_floats);
+    w.plan = plan_attn(B, Hkv, G, n_verify, head_dim, max_list, attn_target_wgs(), split_cap);
+    w.ctr_off = 0;
+    w.part_off = align_up(sizeof(unsigned long long) * w.plan.counters);
+    w.bytes = w.part_off + align_up(sizeof(float) * w.plan.part_floats);
     return w;
 }
 
-// Workspace bytes valid for either table layout (the size queries do not see the views).
-size_t attn_workspace_bytes(int B, int Hq, int Hkv, int n_verify, int max_list)
+// Workspace bytes valid for every table layout (the size queries do not see the views).
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int head_dim, int n_verify, int max_list, bool sparse)
 {
-    return std::max(attn_workspace(B, Hq, Hkv, n_verify, max_list, true).bytes,
-                    attn_workspace(B, Hq, Hkv, n_verify, max_list, false).bytes);
+    size_t m = std::max(attn_workspace(B, Hq, Hkv, head_dim, n_verify, max_list, attn_split_cap(true, false)).bytes,
+                        attn_workspace(B, Hq, Hkv, head_dim, n_verify, max_list, attn_split_cap(true, true)).bytes);
+    if (!sparse)
+        m = std::max(m, attn_workspace(B, Hq, Hkv, head_dim, n_verify, max_list, attn_split_cap(false, false)).bytes);
+    return m;
 }
 
 bool same_rows(const KvView &k, const KvView &v)
 {
     return k.sb == v.sb && k.st == v.st && k.sp == v.sp && k.pt == v.pt && k.ps_log2 == v.ps_log2 &&
            k.max_pages == v.max_pages && k.num_pages == v.num_pages;
+}
+
+// Paged calls keep row numbers (element offset / stride_token) in 32 bits: every offset
+// of the view must be a multiple of stride_token and the largest row number below 2^32.
+bool rows_representable(const KvView &v, int B)
+{
+    if (v.pt)
+        return v.rows_per_page >= 0 && (uint64_t)v.num_pages * (uint64_t)v.rows_per_page + (1ull << v.ps_log2) <= (1ull << 32);
+    return v.rows_per_batch >= 0 && (uint64_t)B * (uint64_t)v.rows_per_batch + (uint64_t)v.cap <= (1ull << 32);
 }
 
 bool attn_shape_ok(int B, int Hq, int Hkv, int head_dim, int n_verify, dustin_status &st)
@@ -153,7 +185,11 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
         return DUSTIN_ERR_UNSUPPORTED;
     const KvView kv = make_view(*k), vv = make_view(*v);
     const bool kv_same = same_rows(kv, vv);
-    const AttnWs lay = attn_workspace(B, Hq, Hkv, n_verify, max_list, kv_same);
+    const bool rows_mode = kv.pt != nullptr || vv.pt != nullptr;
+    if (rows_mode && (!rows_representable(kv, B) || !rows_representable(vv, B)))
+        return DUSTIN_ERR_UNSUPPORTED;
+    const AttnWs lay = attn_workspace(B, Hq, Hkv, head_dim, n_verify, max_list,
+                                      attn_split_cap(sparse || rows_mode, rows_mode && !kv_same));
     if (lay.bytes > 0 && (!ws || ws_bytes < lay.bytes || !aligned16(ws)))
         return DUSTIN_ERR_WORKSPACE;
 
@@ -168,6 +204,7 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
     a.k = kv;
     a.v = vv;
     a.kv_same = kv_same ? 1 : 0;
+    a.rows_mode = rows_mode ? 1 : 0;
     a.ctx_len = ctx_len;
     a.idx = sparse ? idx : nullptr;
     a.count = sparse ? count : nullptr;
@@ -176,14 +213,14 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
     a.scale_log2 = scale * kLog2e;
     a.out = static_cast<uint16_t *>(out);
     a.lse = lse;
+    a.counter = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + lay.ctr_off);
     a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.part_off);
+    a.fused_merge = env_flag("DUSTIN_ATTN_FUSED_MERGE", false) ? 1 : 0;
     a.splits = lay.plan.splits;
     a.spl = lay.plan.spl;
     a.qgroups = lay.plan.qgroups;
     a.pairs = lay.plan.pairs;
-    // LDS ring depth per wave for head dim 64 (head dim 128 always uses two slots)
-    const int ring = env_int("DUSTIN_ATTN_RING", 3);
-    const hipError_t e = launch_attn(a, head_dim, lay.plan.qt, ring, static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_attn(a, head_dim, lay.plan.qt, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
 }
 
@@ -370,7 +407,7 @@ dustin_status dustin_sparse_verify_attn_workspace_size(int B, int Hq, int Hkv, i
         return st;
     if (k_max + n_verify > kMaxList)
         return DUSTIN_ERR_UNSUPPORTED;
-    *bytes = attn_workspace_bytes(B, Hq, Hkv, n_verify, k_max + n_verify);
+    *bytes = attn_workspace_bytes(B, Hq, Hkv, head_dim, n_verify, k_max + n_verify, true);
     return DUSTIN_OK;
 }
 
@@ -397,7 +434,7 @@ dustin_status dense_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_
         return st;
     if (n_max + n_verify > kMaxList)
         return DUSTIN_ERR_UNSUPPORTED;
-    *bytes = attn_workspace_bytes(B, Hq, Hkv, n_verify, n_max + n_verify);
+    *bytes = attn_workspace_bytes(B, Hq, Hkv, head_dim, n_verify, n_max + n_verify, false);
     return DUSTIN_OK;
 }
 

@@ -57,6 +57,8 @@ struct KvView {
     int32_t ps_log2;    // paged: log2(page_size)
     int32_t max_pages;
     int32_t num_pages;
+    int64_t rows_per_batch;   // stride_batch / stride_token (when a multiple)
+    int64_t rows_per_page;    // stride_page / stride_token (when a multiple)
 };
 
 inline KvView make_view(const dustin_kv_view &v)
@@ -71,6 +73,8 @@ inline KvView make_view(const dustin_kv_view &v)
     o.ps_log2 = 0;
     o.max_pages = v.max_pages;
     o.num_pages = v.num_pages;
+    o.rows_per_batch = v.stride_token > 0 && v.stride_batch % v.stride_token == 0 ? v.stride_batch / v.stride_token : -1;
+    o.rows_per_page = v.stride_token > 0 && v.stride_page % v.stride_token == 0 ? v.stride_page / v.stride_token : -1;
     if (v.page_table) {
         while ((1 << o.ps_log2) < v.page_size)
             ++o.ps_log2;

@@ -11,8 +11,11 @@ namespace dustin {
 
 // ---------------------------------------------------------------- attention
 constexpr int kMaxQT = 5;          // 16-row query tiles held by one workgroup
-constexpr int kSplitMax = 2048;    // selected positions of one workgroup (64 steps of 32) when K
-                                   // and V rows share their offsets; half as many when they do not
+constexpr int kAttnStepsMaxW = 16; // 32-position steps of one wave whose list entries (or row
+                                   // numbers) the wave's LDS table holds
+constexpr int kSplitMax = 4 * kAttnStepsMaxW * 32;   // positions of one workgroup when its steps
+                                   // come from the table (sparse lists, paged caches); half as
+                                   // many when K and V rows need a table each
 constexpr int kMaxSplits = 256;    // splits of one (sequence, KV head, query group)
 constexpr int kMaxList = 131072;   // longest list (selected positions + new tokens) accepted
 
@@ -21,6 +24,7 @@ struct AttnArgs {
     const uint16_t *q;
     KvView k, v;
     int kv_same;             // K and V rows of a token sit at the same element offsets
+    int rows_mode;           // K or V paged: rows resolved through the page tables once
     const int32_t *ctx_len;
     const int32_t *idx;      // nullptr = dense: the list is [0, ctx_len[b])
     const int32_t *count;
@@ -30,17 +34,20 @@ struct AttnArgs {
     uint16_t *out;
     float *lse;
     float *part;             // split partials
+    unsigned long long *counter;   // per pair: arrivals of its splits (fused merge)
+    int fused_merge;         // splits merged by their last arrival (else by a second kernel)
     int splits, spl, qgroups, pairs;   // spl: list positions per split; pairs = B*Hkv*qgroups
 };
 
 struct AttnPlan {
     int qt, qgroups, pairs, splits, spl;
-    size_t part_floats;
+    size_t part_floats;      // split partial records
+    size_t counters;         // per-pair arrival counters
     size_t grid;
 };
 
-AttnPlan plan_attn(int B, int Hkv, int G, int nv, int max_list, int target_wgs, int split_cap);
-hipError_t launch_attn(const AttnArgs &a, int head_dim, int qt, int ring, hipStream_t st);
+AttnPlan plan_attn(int B, int Hkv, int G, int nv, int head_dim, int max_list, int target_wgs, int split_cap);
+hipError_t launch_attn(const AttnArgs &a, int head_dim, int qt, hipStream_t st);
 
 // ---------------------------------------------------------------- scoring
 constexpr int kMaxGroups = 16;

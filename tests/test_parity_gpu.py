@@ -256,6 +256,68 @@ def test_k_and_v_at_different_row_offsets():
         check_attn(step.out, step.lse, refd, bs, f"dense, {name}")
 
 
+def _with_env(name, value, fn):
+    old = os.environ.get(name)
+    try:
+        if value is None:
+            os.environ.pop(name, None)
+        else:
+            os.environ[name] = value
+        return fn()
+    finally:
+        if old is None:
+            os.environ.pop(name, None)
+        else:
+            os.environ[name] = old
+
+
+def test_fused_split_merge_matches_merge_kernel_bitwise():
+    """The splits combined inside the attention kernel by the last workgroup to finish equal
+    the separate merge kernel's result bit for bit (same weights, same order), for
+    contiguous and paged caches, sparse and dense, under two split plans; repeated calls
+    on one workspace leave its arrival counters ready for the next call."""
+    from sparse_kv_attention_amd import dustin as D
+    w = small("fused", 3, 2500, 16, 2, 128, 4, 900, 4, 32, 100, seed=23)
+    inp = W.make_inputs(w, device="cuda")
+    step = check_pipeline(inp, [0], [], [0, 2])
+    bs = [0, 1, 2]
+    idx, cnt = step.idx.cpu().numpy(), step.count.cpu().numpy()
+    ref = oracle_attn(inp, 0, idx, cnt, bs)
+    refd = oracle_attn(inp, 0, None, None, bs, dense=True)
+    K, V = inp.k_cache[0], inp.v_cache[0]
+    kp, ptk = _paged_copy(K, 16, 3)
+    vp, ptv = _paged_copy(V, 16, 4)
+    layouts = (("contiguous", (D.kv_view(K), D.kv_view(V))),
+               ("paged, two page tables", (D.kv_view(kp, ptk), D.kv_view(vp, ptv))))
+
+    def run(kv, dense):
+        def go():
+            s2 = step_for(inp, [0])
+            s2.idx.copy_(step.idx)
+            s2.count.copy_(step.count)
+            s2.kv[0] = kv
+            res = []
+            for _ in range(3):
+                s2.dense(0) if dense else s2.attn(0)
+                res.append((s2.out.clone(), s2.lse.clone()))
+            torch.cuda.synchronize()
+            return res
+        return go
+
+    for tw in (None, "7"):
+        for name, kv in layouts:
+            for dense in (False, True):
+                what = f"{'dense' if dense else 'sparse'}, {name}, target wgs {tw or 'default'}"
+                say(f"  fused merge vs merge kernel: {what}")
+                two = _with_env("DUSTIN_ATTN_TARGET_WGS", tw,
+                                lambda: _with_env("DUSTIN_ATTN_FUSED_MERGE", "0", run(kv, dense)))
+                fused = _with_env("DUSTIN_ATTN_TARGET_WGS", tw,
+                                  lambda: _with_env("DUSTIN_ATTN_FUSED_MERGE", "1", run(kv, dense)))
+                for o, l in fused + two[1:]:
+                    assert torch.equal(o, two[0][0]) and torch.equal(l, two[0][1]), what
+                check_attn(fused[0][0], fused[0][1], refd if dense else ref, bs, what)
+
+
 def test_step_replayed_as_hip_graph_matches_eager():
     """The whole step (both scoring calls, selection, two attention layers) captured once as
     a HIP graph: every replay, with eager work and synchronisations in between, gives
