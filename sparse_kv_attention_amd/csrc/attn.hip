@@ -950,6 +950,14 @@ AttnPlan plan_attn(int B, int Hkv, int G, int nv, int head_dim, int max_list, in
     p.qt = (qt_total + qg - 1) / qg;
     p.qgroups = (qt_total + p.qt - 1) / p.qt;
     p.pairs = base * p.qgroups;
+    if (p.pairs <= 0) {               // an empty batch: nothing to launch, no workspace
+        p.spl = kTile;
+        p.splits = 1;
+        p.part_floats = 0;
+        p.counters = 0;
+        p.grid = 0;
+        return p;
+    }
     // Token splits: the minimum, unless the grid would leave more than half of a round
     // idle; then rounded up to whole rounds.
     int s = min_s;

@@ -102,6 +102,10 @@ def test_workspace_queries():
     assert D._sparse_ws(8, 64, 8, 128, 5, 2048, ctypes.byref(n)) == D.OK and n.value > 0
     assert D._dense_ws(8, 64, 8, 128, 5, 32768, ctypes.byref(n)) == D.OK and n.value > 0
     assert D._sparse_ws(8, 64, 8, 96, 5, 2048, ctypes.byref(n)) == D.ERR_UNSUPPORTED
+    n.value = 7
+    assert D._sparse_ws(0, 64, 8, 128, 5, 2048, ctypes.byref(n)) == D.OK and n.value == 0
+    n.value = 7
+    assert D._dense_ws(0, 64, 8, 128, 5, 32768, ctypes.byref(n)) == D.OK and n.value == 0
     assert D._select_ws(8, 32768, ctypes.byref(n)) == D.OK
     assert D._score_ws(8, 32768, 4, 5, D.SCORE_PROB_SUM, ctypes.byref(n)) == D.OK
     assert n.value >= 8 * 20 * 32768 * 4
