@@ -56,7 +56,9 @@ typedef enum {
     DUSTIN_ERR_INVALID_ARG = -1, /* null pointer, bad size, stride or alignment        */
     DUSTIN_ERR_WORKSPACE = -2,   /* workspace missing or smaller than the size query  */
     DUSTIN_ERR_UNSUPPORTED = -3, /* a shape outside what the kernels are built for    */
-    DUSTIN_ERR_HIP = -4          /* the HIP runtime reported an error at launch        */
+    DUSTIN_ERR_HIP = -4,         /* the HIP runtime reported an error at launch        */
+    DUSTIN_ERR_SCRATCH = -5      /* the no-allocation call would need more than the
+                                    library's static scratch array holds               */
 } dustin_status;
 
 /* Scoring modes of dustin_srh_score. */
@@ -190,6 +192,29 @@ dustin_status dustin_sparse_verify_attn(int B, int Hq, int Hkv, int head_dim, in
                                         const int32_t *count, int k_max, float scale,
                                         void *out, float *lse, void *workspace,
                                         size_t workspace_bytes, void *stream);
+
+/* dustin_sparse_verify_attn_noalloc — for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dustin_sparse_verify_attn with the same arguments, results and errors, minus the
+ * workspace.  The split partials and arrival counters live in a static device array of
+ * DUSTIN_NOALLOC_SCRATCH_BYTES inside the library, one per device, held from the first
+ * call on that device until the process ends.  The call allocates nothing.
+ *   - A shape whose dustin_sparse_verify_attn_workspace_size exceeds
+ *     DUSTIN_NOALLOC_SCRATCH_BYTES returns DUSTIN_ERR_SCRATCH and enqueues nothing.
+ *   - The call uses the scratch of the CURRENT device; a non-NULL stream of another
+ *     device returns DUSTIN_ERR_INVALID_ARG.
+ *   - Every call on one device shares that array and leaves the last call's contents in
+ *     it (partials are always written before they are read; the counters are left
+ *     cleared).  Calls that may overlap on one device (different streams, host threads)
+ *     race on it: order them on one stream.
+ */
+#define DUSTIN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+dustin_status dustin_sparse_verify_attn_noalloc(int B, int Hq, int Hkv, int head_dim, int n_verify,
+                                                const void *q, const dustin_kv_view *k /* host */,
+                                                const dustin_kv_view *v /* host */,
+                                                const int32_t *ctx_len, const int32_t *idx,
+                                                const int32_t *count, int k_max, float scale,
+                                                void *out, float *lse, void *stream);
 
 dustin_status dense_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_dim,
                                                int n_verify, int n_max,

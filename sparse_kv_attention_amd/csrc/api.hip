@@ -4,12 +4,19 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "dustin.h"
 #include "kv.hpp"
 #include "launch.hpp"
 
 using namespace dustin;
+
+// The scratch of dustin_sparse_verify_attn_noalloc: a device array in the library's code
+// object (zero at load; each device holds its own copy until the process ends).  Host code
+// never uses the name as an address: the device address comes from hipGetSymbolAddress,
+// taken once per device on the first call made with that device current.
+static __device__ __align__(256) unsigned char scratch[DUSTIN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -158,10 +165,40 @@ bool attn_shape_ok(int B, int Hq, int Hkv, int head_dim, int n_verify, dustin_st
     return true;
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+dustin_status scratch_of_current_device(void *stream, void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return DUSTIN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices)
+        return DUSTIN_ERR_UNSUPPORTED;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+            return DUSTIN_ERR_HIP;
+        if (sdev != dev)
+            return DUSTIN_ERR_INVALID_ARG;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return DUSTIN_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return DUSTIN_OK;
+}
+
 dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const void *q,
                        const dustin_kv_view *k, const dustin_kv_view *v, const int32_t *ctx_len,
                        const int32_t *idx, const int32_t *count, int k_max, int n_max,
-                       float scale, void *out, float *lse, void *ws, size_t ws_bytes, void *stream)
+                       float scale, void *out, float *lse, void *ws, size_t ws_bytes, void *stream,
+                       bool use_scratch = false)
 {
     dustin_status st = DUSTIN_OK;
     if (!attn_shape_ok(B, Hq, Hkv, head_dim, n_verify, st))
@@ -190,6 +227,15 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
         return DUSTIN_ERR_UNSUPPORTED;
     const AttnWs lay = attn_workspace(B, Hq, Hkv, head_dim, n_verify, max_list,
                                       attn_split_cap(sparse || rows_mode, rows_mode && !kv_same));
+    if (use_scratch) {
+        // every host check has passed: only now the scratch of the current device
+        if (lay.bytes > DUSTIN_NOALLOC_SCRATCH_BYTES)
+            return DUSTIN_ERR_SCRATCH;
+        const dustin_status sst = scratch_of_current_device(stream, &ws);
+        if (sst != DUSTIN_OK)
+            return sst;
+        ws_bytes = DUSTIN_NOALLOC_SCRATCH_BYTES;
+    }
     if (lay.bytes > 0 && (!ws || ws_bytes < lay.bytes || !aligned16(ws)))
         return DUSTIN_ERR_WORKSPACE;
 
@@ -271,6 +317,7 @@ const char *dustin_status_string(dustin_status s)
     case DUSTIN_ERR_WORKSPACE: return "workspace missing or too small";
     case DUSTIN_ERR_UNSUPPORTED: return "unsupported shape";
     case DUSTIN_ERR_HIP: return "HIP launch error";
+    case DUSTIN_ERR_SCRATCH: return "needs more than the library's static scratch array";
     }
     return "unknown status";
 }
@@ -422,6 +469,24 @@ dustin_status dustin_sparse_verify_attn(int B, int Hq, int Hkv, int head_dim, in
         return DUSTIN_ERR_INVALID_ARG;
     return run_attn(B, Hq, Hkv, head_dim, n_verify, q, k, v, ctx_len, idx, count, k_max, 0, scale,
                     out, lse, workspace, workspace_bytes, stream);
+}
+
+dustin_status dustin_sparse_verify_attn_noalloc(int B, int Hq, int Hkv, int head_dim, int n_verify,
+                                                const void *q, const dustin_kv_view *k,
+                                                const dustin_kv_view *v, const int32_t *ctx_len,
+                                                const int32_t *idx, const int32_t *count, int k_max,
+                                                float scale, void *out, float *lse, void *stream)
+{
+    size_t need = 0;
+    const dustin_status st = dustin_sparse_verify_attn_workspace_size(B, Hq, Hkv, head_dim, n_verify, k_max, &need);
+    if (st != DUSTIN_OK)
+        return st;
+    if (need > DUSTIN_NOALLOC_SCRATCH_BYTES)
+        return DUSTIN_ERR_SCRATCH;
+    if (!idx || !count)
+        return DUSTIN_ERR_INVALID_ARG;
+    return run_attn(B, Hq, Hkv, head_dim, n_verify, q, k, v, ctx_len, idx, count, k_max, 0, scale,
+                    out, lse, nullptr, 0, stream, true);
 }
 
 dustin_status dense_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_dim, int n_verify,

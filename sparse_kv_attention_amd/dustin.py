@@ -16,7 +16,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdustin.so")
 
-OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP = 0, -1, -2, -3, -4
+OK, ERR_INVALID_ARG, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_HIP, ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 SCORE_PROB_SUM, SCORE_LOGIT_SUM2, SCORE_LOGIT_SUM_ALL = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):
@@ -69,6 +69,9 @@ _sparse_ws = _decl("dustin_sparse_verify_attn_workspace_size", [_I, _I, _I, _I, 
 _sparse = _decl("dustin_sparse_verify_attn", [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView),
                                               ctypes.POINTER(KvView), _P, _P, _P, _I, _F, _P, _P, _P,
                                               _SZ, _P])
+_sparse_noalloc = _decl("dustin_sparse_verify_attn_noalloc",
+                         [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView), ctypes.POINTER(KvView), _P, _P, _P,
+                          _I, _F, _P, _P, _P])
 _dense_ws = _decl("dense_verify_attn_workspace_size", [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)])
 _dense = _decl("dense_verify_attn", [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView),
                                      ctypes.POINTER(KvView), _P, _I, _F, _P, _P, _P, _SZ, _P])
@@ -80,6 +83,7 @@ _recovery = _decl("dustin_attn_recovery", [_I, _P, _P, _P, _P])
 EXPORTED = ("dustin_status_string", "dustin_srh_score_workspace_size", "dustin_srh_score",
             "dustin_select_workspace_size", "dustin_select",
             "dustin_sparse_verify_attn_workspace_size", "dustin_sparse_verify_attn",
+            "dustin_sparse_verify_attn_noalloc",
             "dense_verify_attn_workspace_size", "dense_verify_attn",
             "dustin_kv_write_block", "dustin_kv_commit", "dustin_attn_recovery")
 
@@ -228,6 +232,17 @@ def dustin_sparse_verify_attn(q, k: KvView, v: KvView, Hkv: int, ctx_len, idx, c
     _check(_sparse(B, Hq, Hkv, d, nv, _ptr(q), ctypes.byref(k), ctypes.byref(v), _ptr(ctx_len), _ptr(idx),
                    _ptr(count), idx.shape[1], float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                    _stream(stream)), "dustin_sparse_verify_attn")
+
+
+def dustin_sparse_verify_attn_noalloc(q, k: KvView, v: KvView, Hkv: int, ctx_len, idx, count, scale: float,
+                                      out, lse, stream=None):
+    """dustin_sparse_verify_attn without a workspace: the library's static scratch array of
+    the current device holds the split partials (no device memory is allocated)."""
+    B, nv, Hq, d = _attn_common(q, out, lse)
+    _dev_i32(ctx_len, "ctx_len"); _dev_i32(idx, "idx"); _dev_i32(count, "count")
+    _check(_sparse_noalloc(B, Hq, Hkv, d, nv, _ptr(q), ctypes.byref(k), ctypes.byref(v), _ptr(ctx_len), _ptr(idx),
+                           _ptr(count), idx.shape[1], float(scale), _ptr(out), _ptr(lse), _stream(stream)),
+           "dustin_sparse_verify_attn_noalloc")
 
 
 def dense_verify_attn(q, k: KvView, v: KvView, Hkv: int, ctx_len, n_max: int, scale: float, out, lse, ws,

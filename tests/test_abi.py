@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(D.EXPORTED)
     out = subprocess.run(["nm", "-D", "--defined-only", D.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in (0, -1, -2, -3, -4):
+    for s in (0, -1, -2, -3, -4, -5):
         assert D.status_string(s) and D.status_string(s) != "unknown status"
 
 
@@ -86,6 +86,38 @@ def test_sparse_attn_rejects(kw, status):
 
 def test_zero_batch_is_a_noop():
     assert sparse(B=0, q=None, out=None) == D.OK
+
+
+def noalloc(**kw):
+    a = dict(B=2, Hq=64, Hkv=8, d=128, nv=5, q=FAKE, k=view(), v=view(), ctx=FAKE, idx=FAKE, cnt=FAKE,
+             k_max=256, scale=0.1, out=FAKE, lse=FAKE)
+    a.update(kw)
+    return D._sparse_noalloc(a["B"], a["Hq"], a["Hkv"], a["d"], a["nv"], a["q"], ctypes.byref(a["k"]),
+                             ctypes.byref(a["v"]), a["ctx"], a["idx"], a["cnt"], a["k_max"], a["scale"],
+                             a["out"], a["lse"], None)
+
+
+def scratch_limit():
+    m = re.search(r"#define DUSTIN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", open(HEADER).read())
+    return int(m.group(1)) << int(m.group(2))
+
+
+def test_noalloc_attn_rejects_on_the_host():
+    """The no-allocation variant validates exactly like dustin_sparse_verify_attn, and a
+    shape whose workspace would exceed the static scratch array is refused before the
+    device is touched."""
+    n = ctypes.c_size_t(0)
+    assert D._sparse_ws(64, 64, 8, 128, 9, 4096, ctypes.byref(n)) == D.OK and n.value > scratch_limit()
+    v = view(n_tokens=8192)
+    assert noalloc(B=64, nv=9, k_max=4096, k=v, v=v) == D.ERR_SCRATCH
+    assert D._sparse_ws(8, 64, 8, 128, 5, 2048, ctypes.byref(n)) == D.OK and 0 < n.value <= scratch_limit()
+    for kw, status in [(dict(d=96), D.ERR_UNSUPPORTED), (dict(Hq=60), D.ERR_INVALID_ARG),
+                       (dict(q=None), D.ERR_INVALID_ARG), (dict(q=FAKE + 2), D.ERR_INVALID_ARG),
+                       (dict(idx=None), D.ERR_INVALID_ARG), (dict(cnt=None), D.ERR_INVALID_ARG),
+                       (dict(k_max=-1), D.ERR_INVALID_ARG), (dict(scale=float("nan")), D.ERR_INVALID_ARG),
+                       (dict(k=view(stride_token=1001)), D.ERR_INVALID_ARG), (dict(out=None), D.ERR_INVALID_ARG)]:
+        assert noalloc(**kw) == status, kw
+    assert noalloc(B=0, q=None, out=None) == D.OK
 
 
 def test_dense_rejects():
