@@ -11,8 +11,8 @@
  *                             selected tokens only
  *   dense_verify_attn         the full-cache verification it replaces ("Problem
  *                             Statement": the target loads the full KV cache)
- *   dustin_kv_write_block,    step 5: the verified block in the cache; accepted tokens
- *   dustin_kv_commit          are kept, rejected ones discarded
+ *   dustin_kv_write_block,    step 5: the verified block in the cache, and the cache
+ *   dustin_kv_commit          length advanced over the drafts the target kept
  *   dustin_attn_recovery      the share of full-cache attention mass the kept set
  *                             carries ("Methodology" 2: attention recovery rate)
  *
@@ -126,7 +126,7 @@ const char *dustin_status_string(dustin_status s);
  *   scale  : any finite value (0 and negative included); non-finite -> INVALID_ARG
  *   head_dim in {64, 128}; 1 <= n_q <= 16; pairs per group (n_qheads * queries used)
  *   at most 16 in PROB_SUM mode and 64 in the logit-sum modes
- *   score  : fp32 [B][n_max], fully written
+ *   score  : fp32 [B][n_max], fully written; 16-byte aligned (else INVALID_ARG)
  *   workspace: at least dustin_srh_score_workspace_size(...) bytes, any contents
  * ------------------------------------------------------------------------------- */
 dustin_status dustin_srh_score_workspace_size(int B, int n_max, int total_qheads, int n_q,
@@ -152,6 +152,7 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
  *   idx   : int32 [B][k_max] ascending positions, entries count[b].. set to -1
  *   count : int32 [B] = |I|
  *   budget, n_sink, n_window, m : int32 [B] (negative values act as 0)
+ *   score_draft, score_target : fp32 [B][n_max], 16-byte aligned (else INVALID_ARG)
  *   n_max <= 65536.  workspace: dustin_select_workspace_size(...) bytes (may be 0).
  * ------------------------------------------------------------------------------- */
 dustin_status dustin_select_workspace_size(int B, int n_max, size_t *bytes /* host */);
@@ -227,7 +228,7 @@ dustin_status dense_verify_attn(int B, int Hq, int Hkv, int head_dim, int n_veri
 
 /* ---------------------------------------------------------------------------------
  * Step 5 — the verified block in the cache (English Dustin summary, Verification
- * Workflow step 5: accepted tokens are appended to the cache, rejected ones discarded).
+ * Workflow step 5: the cache after the target's decision on the drafts).
  *
  * dustin_kv_write_block stores the block being verified behind the committed context,
  * where dustin_sparse_verify_attn and dense_verify_attn read the new tokens:

@@ -346,7 +346,7 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
         return DUSTIN_ERR_UNSUPPORTED;
     if (B == 0 || n_max == 0)
         return DUSTIN_OK;
-    if (!ctx_len || !q || !score || !aligned16(q))
+    if (!ctx_len || !q || !score || !aligned16(q) || !aligned16(score))
         return DUSTIN_ERR_INVALID_ARG;
     const int ppq = pairs_per_qhead(n_q, mode);
     int total_qheads = 0, max_pairs = 0, ctx_clamp = n_max;
@@ -426,6 +426,9 @@ dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const floa
         return DUSTIN_OK;
     if (!ctx_len || !score_target || !budget || !n_sink || !n_window || !m || !count ||
         (k_max > 0 && !idx))
+        return DUSTIN_ERR_INVALID_ARG;
+    // the kernels read score rows as 16-byte vectors
+    if (!aligned16(score_target) || (score_draft && !aligned16(score_draft)))
         return DUSTIN_ERR_INVALID_ARG;
     SelectArgs a;
     a.B = B;

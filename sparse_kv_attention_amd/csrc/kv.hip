@@ -1,7 +1,7 @@
 // The verified block in the cache, and attention recovery.
 //
-// English Dustin summary, Verification Workflow step 5: accepted tokens are appended to
-// the cache and rejected tokens discarded.  The block being verified is stored behind
+// English Dustin summary, Verification Workflow step 5 (what happens to the cache once
+// the target has decided which drafts it keeps).  The block being verified is stored behind
 // the committed context (where the verification attention reads the new tokens); the
 // commit advances each sequence's length over the rows that are kept, and the rows
 // behind the new length are simply overwritten by the next block.  Both are pure data

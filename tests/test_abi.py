@@ -167,6 +167,7 @@ def test_score_rejects():
         assert f(scale=bad_scale) == D.ERR_INVALID_ARG
     assert f(q=None) == D.ERR_INVALID_ARG
     assert f(score=None) == D.ERR_INVALID_ARG
+    assert f(score=FAKE + 4) == D.ERR_INVALID_ARG      # fp32 rows are written as 16-byte vectors
     assert f(ws=None) == D.ERR_WORKSPACE
     assert f(wsb=100) == D.ERR_WORKSPACE
     bad = (D.SrhGroup * 1)()
@@ -187,8 +188,10 @@ def test_score_rejects():
 
 
 def test_select_rejects():
-    f = lambda **kw: D._select(2, kw.get("n_max", 4096), FAKE, FAKE, kw.get("st", FAKE), FAKE, FAKE, FAKE,
-                               FAKE, kw.get("k_max", 256), kw.get("idx", FAKE), FAKE, None, 0, None)
+    f = lambda **kw: D._select(2, kw.get("n_max", 4096), FAKE, kw.get("sd", FAKE), kw.get("st", FAKE), FAKE, FAKE,
+                               FAKE, FAKE, kw.get("k_max", 256), kw.get("idx", FAKE), FAKE, None, 0, None)
+    assert f(st=FAKE + 4) == D.ERR_INVALID_ARG        # scores are read as 16-byte vectors
+    assert f(sd=FAKE + 8) == D.ERR_INVALID_ARG
     assert f(n_max=65537) == D.ERR_UNSUPPORTED
     assert f(st=None) == D.ERR_INVALID_ARG
     assert f(idx=None) == D.ERR_INVALID_ARG
