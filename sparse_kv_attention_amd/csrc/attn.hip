@@ -255,6 +255,14 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
     constexpr int R = S::R;
     __shared__ __align__(16) uint8_t lds[S::LDS];
 
+    // The argument fields the prologue and the ring need, requested from the kernel
+    // argument segment in one batch with one wait (left to itself the compiler loads each
+    // where it is first used, one dependent round trip after another).
+    asm volatile("" ::"s"(a.B), "s"(a.Hkv), "s"(a.qgroups), "s"(a.splits), "s"(a.spl), "s"(a.GV), "s"(a.G),
+                 "s"(a.nv), "s"(a.Hq), "s"(a.q), "s"(a.idx), "s"(a.count), "s"(a.ctx_len), "s"(a.k_max),
+                 "s"(a.k.base), "s"(a.k.sb), "s"(a.k.st), "s"(a.k.sh), "s"(a.v.base), "s"(a.v.sb), "s"(a.v.st),
+                 "s"(a.v.sh), "s"(a.kv_same), "s"(a.rows_mode), "s"(a.ctx_clamp));
+
     // ---- block -> (sequence, KV head, query group, split).  Every workgroup of one
     //      (sequence, KV head) has the same blockIdx % 8, i.e. runs on the same XCD ----
     const int x = blockIdx.x;
@@ -279,9 +287,13 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
     const int p0 = split * a.spl;
     const bool sparse = a.idx != nullptr;
 
-    // ---- per-sequence values ----
-    const int n_raw = __builtin_amdgcn_readfirstlane(a.ctx_len[b]);
-    const int c_raw = sparse ? __builtin_amdgcn_readfirstlane(a.count[b]) : 0;
+    // ---- per-sequence values, as vector loads (an opaque zero index keeps them off the
+    //      scalar path) so they travel in the same round trip as Q and the list entries:
+    //      a scalar load here would cost its own round trip before the first DMA ----
+    int zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+    const int n_v = a.ctx_len[b + zero];
+    const int c_v = sparse ? a.count[b + zero] : 0;
 
     // ---- Q of the query group into the ring area (not yet in use) by LDS DMA, a quarter
     //      of the rows per wave, chunk c of row r at c ^ (r % CPR); padding rows copy the
@@ -337,8 +349,8 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
                 lds + (qt * 16 + li) * G::RB + (((ks * 4 + quad) ^ ((qt * 16 + li) % G::CPR)) << 4));
 
     // ---- sequence geometry; every device value is clamped ----
-    const int N = clampi(n_raw, 0, a.ctx_clamp);
-    const int nsel = sparse ? clampi(c_raw, 0, min(a.k_max, N)) : N;
+    const int N = clampi(__builtin_amdgcn_readfirstlane(n_v), 0, a.ctx_clamp);
+    const int nsel = sparse ? clampi(__builtin_amdgcn_readfirstlane(c_v), 0, min(a.k_max, N)) : N;
     const int p1 = min(p0 + a.spl, nsel);
     const int cnt = max(p1 - p0, 0);
     const int ntile = (cnt + kTile - 1) / kTile;
