@@ -9,13 +9,10 @@
 //                    claims 64-token tiles from the workgroup's counter, reads a tile's
 //                    key rows with coalesced non-temporal 16-byte loads into its own LDS
 //                    area, and keeps the next tile in flight in registers; no workgroup
-//                    barrier is taken per tile.  The lanes of a token group share tokens
-//                    and split the head dim, so each fp64 query value read from LDS
-//                    feeds several tokens; the group's partial dot products are combined by
-//                    a DPP reduce-scatter, after which lane t holds token t of the tile.
-//                    Products of bf16 values are exact in fp64, so the only rounding is
-//                    fp64 accumulation.  Logits are stored as fp32 offsets from the maximum
-//                    of their 64-token statistics tile (one wave), so tokens near the
+//                    barrier is taken per tile.  Dot products run on the matrix cores
+//                    (bf16 in, one fp32 sum per 32-element chunk of the head dim, the
+//                    chunks added in fp64).  Logits are stored as fp32 offsets from the
+//                    maximum of their 64-token statistics tile, so tokens near the
 //                    maximum — the ones that carry probability mass — keep full relative
 //                    precision even when logits are large.  Every tile leaves its maximum
 //                    and sum of exp2 per pair; every workgroup folds its tiles, in tile
@@ -69,38 +66,6 @@ __device__ __forceinline__ double swap_max_f64(double v, bool wide)
     return fmax(x, y);
 }
 
-// In-place whole-wave max (MAX) or sum of N values per lane, all values through each step
-// together; every lane ends with the results.
-template <int N, bool MAX>
-__device__ __forceinline__ void wave_reduce_f32(float (&v)[N])
-{
-    auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        v[i] = op(v[i], __uint_as_float(dpp32<0xB1>(__float_as_uint(v[i]))));
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        v[i] = op(v[i], __uint_as_float(dpp32<0x4E>(__float_as_uint(v[i]))));
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        v[i] = op(v[i], __uint_as_float(dpp32<0x141>(__float_as_uint(v[i]))));
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-        v[i] = op(v[i], __uint_as_float(dpp32<0x140>(__float_as_uint(v[i]))));
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const uint32_t u = __float_as_uint(v[i]);
-        const auto t = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        v[i] = op(__uint_as_float(t[0]), __uint_as_float(t[1]));
-    }
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        const uint32_t u = __float_as_uint(v[i]);
-        const auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        v[i] = op(__uint_as_float(t[0]), __uint_as_float(t[1]));
-    }
-}
-
 // In-place max (MAX) or sum over each 16-lane row of N values per lane; every lane of a
 // row ends with its row's results.
 template <int N, bool MAX>
@@ -131,55 +96,48 @@ __device__ __forceinline__ double wave_max_f64_dpp(double v)
     return swap_max_f64(v, true);
 }
 
-// v from the lane whose index differs in bit log2(X) (X = 1 or 2), within the quad
-template <int X>
-__device__ __forceinline__ double quad_xor(double v)
-{
-    constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
-    const uint64_t u = __double_as_longlong(v);
-    const int lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, ctrl, 0xF, 0xF, true);
-    const int hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), ctrl, 0xF, 0xF, true);
-    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
-}
+// Waves per workgroup of the softmax-mode logit kernel: two per SIMD.  One workgroup
+// fills a CU, so all of a CU's waves draw tiles from one counter and none is left running
+// alone at the end.
+constexpr int kProbWaves = 8;
 
-// Waves per workgroup of the softmax-mode logit kernel.  One workgroup fills a CU, so all
-// of a CU's waves draw tiles from one counter and none is left running alone at the end.
-// Two waves per SIMD fit every variant's registers but the paged one for groups of more
-// than 8 pairs at head dim 128, which would spill and runs one wave per SIMD instead.
-// (Three per SIMD, possible for the 140-register matrix-core variant, measured slower:
-// the third wave's tiles only add to the requests queued at the start.)
-template <int D, int PC, bool FLAT>
-constexpr int prob_waves()
+// The 32-lane halves of a wave exchanged (permlane32 swap), then the 16-lane rows within
+// each half (permlane16 swap): combines the four lanes l % 16 + 16 k, for N values per
+// lane; every lane ends with its column's results.
+template <int N, bool MAX>
+__device__ __forceinline__ void column_reduce_f32(float (&v)[N])
 {
-    return (PC > 8 && D == 128 && !FLAT) ? 4 : 8;
+    auto op = [](float x, float y) { return MAX ? fmaxf(x, y) : x + y; };
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t u = __float_as_uint(v[i]);
+        const auto t = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        v[i] = op(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const uint32_t u = __float_as_uint(v[i]);
+        const auto t = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        v[i] = op(__uint_as_float(t[0]), __uint_as_float(t[1]));
+    }
 }
 
 // FLAT: every group's view is unpaged with a row stride below 4 GiB, so a row address is a
 // per-workgroup base plus token x stride (one 32x32->64 multiply-add per load).
-template <int D, int PC, bool FLAT>
-__global__ __launch_bounds__((64 * prob_waves<D, PC, FLAT>()))
-__attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_prob_logits_kernel(ScoreArgs a)
+template <int D, bool FLAT>
+__global__ __launch_bounds__(64 * kProbWaves)
+__attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel(ScoreArgs a)
 {
-    constexpr int NW = prob_waves<D, PC, FLAT>();
+    constexpr int NW = kProbWaves;
     constexpr int NT = 64 * NW;
-    // groups of 4 pairs: the dot products run on the fp64 matrix cores
-    constexpr bool MF = PC == 4;
-    // lanes per token group = tokens per lane: 4 where registers allow (each query value
-    // then feeds four tokens), 2 for the 128-wide rows (two tiles of them are in flight)
-    constexpr int S = (D > 64 || PC > 8) ? 2 : 4;
-    constexpr int KT = S;                  // tokens converted to fp64 at once
-    // tiles in flight in registers per wave: two where the registers hold them (row
-    // addresses are then one multiply-add each), else one.  Four 8 KB tiles fit the
-    // matrix-core variant at head dim 64 but measured slower: they only lengthen the queue
-    // of requests every wave issues at the start.
-    constexpr int kDepth = (FLAT && (D == 64 || PC <= 5)) ? 2 : 1;
-    constexpr int RB = D * 2;          // bytes per key row
-    constexpr int RSTR = RB + 16;      // LDS row stride (conflict-free 16-byte row reads)
-    constexpr int CPR = RB / 16;       // 16-byte chunks per row
+    constexpr int KS = D / 32;          // MFMA k-steps of a row (32 elements each)
+    constexpr int kDepth = FLAT ? 2 : 1;   // tiles in flight in registers per wave
+    constexpr int RB = D * 2;           // bytes per key row
+    constexpr int RSTR = RB + 16;       // LDS row stride (conflict-free 16-byte row reads)
+    constexpr int CPR = RB / 16;        // 16-byte chunks per row
     constexpr int LPT = kStatTile * CPR / 64;   // 16-byte loads per lane per 64-token tile
     __shared__ __align__(16) uint8_t sK[NW][kStatTile * RSTR];   // one tile per wave
-    __shared__ __align__(16) double sQ[PC][D];
-    __shared__ int sNext;              // tiles claimed so far by the workgroup's waves
+    __shared__ int sNext;               // tiles claimed so far by the workgroup's waves
 
     const ScoreGroup &G = a.grp[blockIdx.y];
     const int b = blockIdx.z;
@@ -187,6 +145,8 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_p
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
+    const int quad = lane >> 4;
+    const int li = lane & 15;
     // 64-token tiles holding context tokens; this workgroup takes an equal share of them
     const int n_live = (N + kStatTile - 1) / kStatTile;
     const int q_lo = (int)((int64_t)n_live * blockIdx.x / gridDim.x);
@@ -206,28 +166,31 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_p
         }
         return;
     }
-    // the group's queries (fp64) stay in LDS for every tile of this workgroup
-    for (int e = tid; e < PC * D; e += NT) {
-        const int p = e / D;
-        const int dd = e - p * D;
-        double qv = 0.0;
+    // The group's queries as the MFMA B operand, in registers for every tile: lane holds
+    // pair li (zero past the group's pairs), head-dim elements 32 ks + 8 quad .. +8
+    u32x4 qop[KS];
+    {
+        const int p = li;
+        const uint16_t *qp = nullptr;
         if (p < G.n_pairs) {
             const int hl = p / a.n_q;
             const int j = p - hl * a.n_q;
-            const uint16_t h = a.q[((int64_t)(b * a.total_qheads + G.q_head0 + hl) * a.n_q + j) * D + dd];
-            qv = (double)__uint_as_float((uint32_t)h << 16);
+            qp = a.q + ((int64_t)(b * a.total_qheads + G.q_head0 + hl) * a.n_q + j) * D + quad * 8;
         }
-        sQ[p][dd] = qv;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qop[ks] = qp ? load16(qp + ks * 32) : u32x4{0, 0, 0, 0};
     }
     if (tid == 0)
         sNext = 0;
-    __syncthreads();                  // queries and the tile counter ready
+    __syncthreads();                  // the tile counter ready
     uint8_t *myK = sK[w];
 
     // A wave's tile is 64 tokens: lane l loads chunks l + 64 i (row = chunk / CPR) of the
-    // tile's rows, all issued at once, kDepth tiles in flight in registers per lane.  Loads
-    // are unconditional (positions past the context, and tiles past the workgroup's share,
-    // read row N-1, which is discarded), so the waits count exactly.
+    // tile's rows (whole rows per instruction: the coalescing the matrix-core operand
+    // layout would not give), all issued at once, kDepth tiles in flight in registers per
+    // lane.  Loads are unconditional (positions past the context, and tiles past the
+    // workgroup's share, read row N-1, which is discarded), so the waits count exactly.
     const char *flat_base = reinterpret_cast<const char *>(G.k.base + (int64_t)b * G.k.sb + (int64_t)G.kv_head * G.k.sh) +
                             (lane % CPR) * 16;
     const uint32_t flat_st = (uint32_t)(G.k.st * 2);
@@ -266,180 +229,70 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_p
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         __builtin_amdgcn_wave_barrier();
     };
+    // One staged 64-token tile.  Dot products on the matrix cores: row block rb (16
+    // tokens) times the 16 pairs, one v_mfma_f32_16x16x32_bf16 per 32-element chunk of the
+    // head dim, each from a zero accumulator; the chunk sums are added in fp64.  The bf16
+    // products are exact in fp32 and the instruction rounds each 32-term sum once (terms
+    // far below its largest product can be dropped), so a logit's error is a few fp32 ulps
+    // of its largest 32-term partial sum.  Lane l ends with pair l % 16 of tokens
+    // 16 rb + 4 (l / 16) + r, r < 4.
     auto process = [&](int tile) {
-        // Dot products: S lanes share the S tokens S*g .. S*g+S-1 and split the head dim,
-        // lane s taking the 16-byte chunks S*j+s (so the 16 lanes of an LDS pass hit
-        // distinct banks).  Each query value read from LDS feeds KT tokens.
-        const int g = lane / S;
-        const int s = lane % S;
-        double acc[S][PC];
+        double lg[4][4];
 #pragma unroll
-        for (int i = 0; i < S; ++i)
+        for (int rb = 0; rb < 4; ++rb) {
+            f32x4 c[KS];
 #pragma unroll
-            for (int p = 0; p < PC; ++p)
-                acc[i][p] = 0.0;
-#pragma unroll 1
-        for (int j = 0; j < CPR / S; ++j) {
-            const int ch = S * j + s;
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 kop = *reinterpret_cast<const u32x4 *>(&myK[(16 * rb + li) * RSTR + (ks * 4 + quad) * 16]);
+                c[ks] = mfma_bf16(kop, qop[ks], f32x4{0.f, 0.f, 0.f, 0.f});
+            }
 #pragma unroll
-            for (int i0 = 0; i0 < S; i0 += KT) {
-                double kv[KT][8];
+            for (int r = 0; r < 4; ++r) {
+                double v = (double)c[0][r];
 #pragma unroll
-                for (int i = 0; i < KT; ++i) {
-                    const u32x4 kw = *reinterpret_cast<const u32x4 *>(&myK[(S * g + i0 + i) * RSTR + ch * 16]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        kv[i][2 * e] = (double)bf16_lo(kw[e]);
-                        kv[i][2 * e + 1] = (double)bf16_hi(kw[e]);
-                    }
-                }
-#pragma unroll
-                for (int p = 0; p < PC; ++p) {
-                    double qv[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        qv[e] = sQ[p][8 * ch + e];
-#pragma unroll
-                    for (int i = 0; i < KT; ++i)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            acc[i0 + i][p] = fma(kv[i][e], qv[e], acc[i0 + i][p]);
-                    __builtin_amdgcn_sched_barrier(0);   // keep one pair's query values live at a time
-                }
+                for (int ks = 1; ks < KS; ++ks)
+                    v += (double)c[ks][r];
+                lg[rb][r] = v;
             }
         }
-        // reduce-scatter over the S lanes: lane s ends with the full sums of token S*g+s,
-        // i.e. lane l holds token l of the tile
-        const int tok = tile * kStatTile + lane;
-        const bool valid = tok < N;
-        double l[PC];
-#pragma unroll
-        for (int p = 0; p < PC; ++p) {
-            double keep[2];
-            if constexpr (S == 4) {
-                const bool hi2 = s & 2;
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const double mine = hi2 ? acc[2 + k][p] : acc[k][p];
-                    const double give = hi2 ? acc[k][p] : acc[2 + k][p];
-                    keep[k] = mine + quad_xor<2>(give);
-                }
-            } else {
-                keep[0] = acc[0][p];
-                keep[1] = acc[1][p];
-            }
-            const bool hi1 = s & 1;
-            const double mine = hi1 ? keep[1] : keep[0];
-            const double give = hi1 ? keep[0] : keep[1];
-            l[p] = mine + quad_xor<1>(give);
-        }
-
-        // ---- the wave's 64 tokens are one statistics tile: per-pair maximum, offsets from
-        // it, sum of exp2.  The maximum is taken over the fp32-rounded logits (rounding is
-        // monotonic, so it is the rounded true maximum); it is the tile's reference and the
-        // offsets are formed against it in fp64.  All pairs go through each reduction step
-        // together. ----
-        const int stile = tile;
-        double lp[PC];
-        float mf[PC], off[PC], ex[PC];
-#pragma unroll
-        for (int p = 0; p < PC; ++p) {
-            lp[p] = valid ? l[p] * a.mul : -INFINITY;
-            mf[p] = (float)lp[p];
-        }
-        wave_reduce_f32<PC, true>(mf);
-#pragma unroll
-        for (int p = 0; p < PC; ++p) {
-            off[p] = valid ? (float)(lp[p] - (double)mf[p]) : -INFINITY;
-            ex[p] = valid ? fast_exp2(off[p]) : 0.f;
-        }
-        wave_reduce_f32<PC, false>(ex);
-        const int64_t row0 = (int64_t)b * a.total_pairs + G.pair0;
-#pragma unroll
-        for (int p = 0; p < PC; ++p)
-            if (p < G.n_pairs && valid)
-                a.logits[(row0 + p) * a.n_pad + tok] = off[p];
-        // lane p < PC takes pair p: it stores the tile's maximum and sum of exp2
-        float m_l = mf[0], s_l = ex[0];
-#pragma unroll
-        for (int p = 1; p < PC; ++p) {
-            m_l = lane == p ? mf[p] : m_l;
-            s_l = lane == p ? ex[p] : s_l;
-        }
-        if (lane < G.n_pairs && lane < PC && stile < a.n_tiles) {
-            a.tile_max[(row0 + lane) * a.n_tiles + stile] = (double)m_l;
-            a.tile_sum[(row0 + lane) * a.n_tiles + stile] = (double)s_l;
-        }
-    };
-
-    // Matrix-core path (groups of 4 pairs).  Block b (of 4) of v_mfma_f64_4x4x4f64 computes
-    // C[i][j] += sum_k A[i][k] B[k][j] with A[i][k] at lane 16k + 4b + i, B[k][j] at lane
-    // 16k + 4b + j and C[i][j] at lane 16i + 4b + j (lane layout measured on the GPU).
-    // Rows i are the pairs, columns j tokens, and step s covers the head-dim elements
-    // (D/4) k + s, the same order for Q and K; one instruction covers 16 tokens (4 blocks
-    // x 4), so a wave's 64 tokens are four accumulators.  Products of bf16 values are exact
-    // in fp64.  After the products, lane l holds pair l/16 of token l%16 of each 16-token
-    // group, so every per-pair reduction stays within a 16-lane row, and pair p keeps its
-    // running (max, sum) in lane 16p.  The fp64 matrix rate equals the vector rate on this
-    // part; the gain is in the query reads (one per 16 tokens) and the reduce-scatter that
-    // is no longer needed.  A fifth pair on the vector unit made 5-pair groups slower.
-    auto process_mf = [&](auto tile) {   // generic: only instantiated where it is called
-        constexpr int DK = D / 4;
-        const int kq = lane >> 4;
-        const int t16 = lane & 15;
-        const double *qa_row = &sQ[lane & 3][kq * DK];
-        const uint8_t *k_row = &myK[t16 * RSTR + kq * DK * 2];
-        double cm[4] = {0.0, 0.0, 0.0, 0.0};
-        // 8 head-dim elements (one 16-byte LDS read per token) at a time
-#pragma unroll 1
-        for (int c = 0; c < DK / 8; ++c) {
-            u32x4 kraw[4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g)
-                kraw[g] = *reinterpret_cast<const u32x4 *>(k_row + 16 * g * RSTR + c * 16);
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const double qa = qa_row[8 * c + s];
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint32_t wd = kraw[g][s / 2];
-                    const double kv = (double)((s & 1) ? bf16_hi(wd) : bf16_lo(wd));
-                    cm[g] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa, kv, cm[g], 0, 0, 0);
-                }
-            }
-        }
-        // statistics of the wave's 64 tokens (one statistics tile) per pair: the maximum of
-        // the fp32-rounded logits as the tile's reference, offsets against it, sum of exp2
-        const int stile = tile;
-        const int tok0 = tile * kStatTile + t16;               // + 16 g
-        const int pr = lane >> 4;                              // the lane's pair
-        double lm[4];
+        // ---- the 64 tokens are one statistics tile: per pair, the maximum of the
+        // fp32-rounded logits (rounding is monotonic, so it is the rounded true maximum)
+        // as the tile's reference, offsets against it formed in fp64, sum of exp2 ----
+        const int tok0 = tile * kStatTile + 4 * quad;          // + 16 rb + r
+        double lp[4][4];
         float red[1] = {-INFINITY};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            lm[g] = tok0 + 16 * g < N ? cm[g] * a.mul : -INFINITY;
-            red[0] = fmaxf(red[0], (float)lm[g]);
-        }
-        row16_reduce_f32<1, true>(red);
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                lp[rb][r] = tok0 + 16 * rb + r < N ? lg[rb][r] * a.mul : -INFINITY;
+                red[0] = fmaxf(red[0], (float)lp[rb][r]);
+            }
+        column_reduce_f32<1, true>(red);
         const float mx = red[0];
-        float off[4];
+        float off[4][4];
         red[0] = 0.f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const bool vld = tok0 + 16 * g < N;
-            off[g] = vld ? (float)(lm[g] - (double)mx) : -INFINITY;
-            red[0] += vld ? fast_exp2(off[g]) : 0.f;
-        }
-        row16_reduce_f32<1, false>(red);
-        const int64_t row0 = (int64_t)b * a.total_pairs + G.pair0;
-        if (pr < G.n_pairs) {
+        for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                if (tok0 + 16 * g < N)
-                    a.logits[(row0 + pr) * a.n_pad + tok0 + 16 * g] = off[g];
-            if (t16 == 0 && stile < a.n_tiles) {
-                a.tile_max[(row0 + pr) * a.n_tiles + stile] = (double)mx;
-                a.tile_sum[(row0 + pr) * a.n_tiles + stile] = (double)red[0];
+            for (int r = 0; r < 4; ++r) {
+                const bool vld = tok0 + 16 * rb + r < N;
+                off[rb][r] = vld ? (float)(lp[rb][r] - (double)mx) : -INFINITY;
+                red[0] += vld ? fast_exp2(off[rb][r]) : 0.f;
+            }
+        column_reduce_f32<1, false>(red);
+        if (li < G.n_pairs) {
+            const int64_t row = (int64_t)b * a.total_pairs + G.pair0 + li;
+            // four consecutive tokens per store; tok0 + 16 rb < N <= n_pad, both multiples
+            // of four, so the four stay inside the row
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                if (tok0 + 16 * rb < N)
+                    *reinterpret_cast<f32x4 *>(a.logits + row * a.n_pad + tok0 + 16 * rb) =
+                        f32x4{off[rb][0], off[rb][1], off[rb][2], off[rb][3]};
+            if (quad == 0 && tile < a.n_tiles) {
+                a.tile_max[row * a.n_tiles + tile] = (double)mx;
+                a.tile_sum[row * a.n_tiles + tile] = (double)red[0];
             }
         }
     };
@@ -468,12 +321,8 @@ __attribute__((amdgpu_waves_per_eu((prob_waves<D, PC, FLAT>() / 4)))) void srh_p
             stage(kr[d]);
             const int nq = claim();
             issue(kr[d], nq);
-            if (d == 0 || qs[d] < q_hi) {
-                if constexpr (MF)
-                    process_mf(qs[d]);
-                else
-                    process(qs[d]);
-            }
+            if (d == 0 || qs[d] < q_hi)
+                process(qs[d]);
             qs[d] = nq;
         }
     }
@@ -719,19 +568,17 @@ hipError_t launch_logit_sum(const ScoreArgs &a, int pt, dim3 grid, hipStream_t s
     return hipGetLastError();
 }
 
-// The softmax-mode kernel, instantiated for the pair counts of one group.  Its grid is one
-// resident round: as many workgroups per CU as the variant's registers and LDS allow (asked
-// of the runtime once per variant), each taking an equal share of its stream's tiles.
-// a.n_parts comes in as the workspace's maximum and leaves as the count launched (the
-// finalize reads that many).
-template <int D, int PC, bool FLAT>
+// The softmax-mode kernel.  Its grid is one resident round: as many workgroups per CU as
+// the variant's registers and LDS allow (asked of the runtime once per variant), each
+// taking an equal share of its stream's tiles.  a.n_parts comes in as the workspace's
+// maximum and leaves as the count launched (the finalize reads that many).
+template <int D, bool FLAT>
 hipError_t launch_prob_variant(ScoreArgs &a, int cus, hipStream_t st)
 {
-    constexpr int nt = 64 * prob_waves<D, PC, FLAT>();
+    constexpr int nt = 64 * kProbWaves;
     static const int per_cu = [] {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, srh_prob_logits_kernel<D, PC, FLAT>, nt, 0) !=
-                hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, srh_prob_logits_kernel<D, FLAT>, nt, 0) != hipSuccess ||
             n < 1)
             n = 1;
         return n;
@@ -739,30 +586,19 @@ hipError_t launch_prob_variant(ScoreArgs &a, int cus, hipStream_t st)
     const int ws = a.n_groups * a.B;
     a.n_parts = std::max(1, std::min(a.n_parts, (per_cu * cus + ws - 1) / ws));
     const dim3 grid((unsigned)a.n_parts, (unsigned)a.n_groups, (unsigned)a.B);
-    hipLaunchKernelGGL((srh_prob_logits_kernel<D, PC, FLAT>), grid, dim3(nt), 0, st, a);
+    hipLaunchKernelGGL((srh_prob_logits_kernel<D, FLAT>), grid, dim3(nt), 0, st, a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_prob(ScoreArgs &a, int max_pairs, int cus, hipStream_t st)
 {
+    if (max_pairs > 16)
+        return hipErrorInvalidValue;
     bool flat = true;
     for (int g = 0; g < a.n_groups; ++g)
         flat = flat && !a.grp[g].k.pt && a.grp[g].k.st >= 0 && a.grp[g].k.st * 2 < (int64_t)1 << 32;
-#define DUSTIN_PROB(PCV) \
-    return flat ? launch_prob_variant<D, PCV, true>(a, cus, st) : launch_prob_variant<D, PCV, false>(a, cus, st)
-    if (max_pairs <= 4)
-        DUSTIN_PROB(4);
-    if (max_pairs <= 5)
-        DUSTIN_PROB(5);
-    if (max_pairs <= 8)
-        DUSTIN_PROB(8);
-    if (max_pairs <= 12)
-        DUSTIN_PROB(12);
-    if (max_pairs <= 16)
-        DUSTIN_PROB(16);
-#undef DUSTIN_PROB
-    return hipErrorInvalidValue;
+    return flat ? launch_prob_variant<D, true>(a, cus, st) : launch_prob_variant<D, false>(a, cus, st);
 }
 
 }  // namespace
