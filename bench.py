@@ -90,7 +90,8 @@ def main():
     ap.add_argument("--layers", type=int, default=80, help="target layers (80 = the whole 72B-shaped model)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle sample")
-    ap.add_argument("--dense-layers", type=int, default=8)
+    ap.add_argument("--dense-layers", type=int, default=80,
+                    help="layers of dense attention timed (all of them by default)")
     ap.add_argument("--counters", action="store_true", help="calibration copy + attention calls only")
     ap.add_argument("--estimator-sweep", action="store_true",
                     help="naive all-heads estimator vs dense attention vs SRH scoring, context 1k..64k")
@@ -150,18 +151,19 @@ def main():
     torch.cuda.synchronize()
     counts = step.count.cpu().tolist()
 
-    # ---- timed steps ----
+    # ---- timed steps (an event between consecutive steps gives each step's time) ----
     ev = lambda: torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    e0, e1 = ev(), ev()
+    evs_step = [ev() for _ in range(args.steps + 1)]
     t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
+    evs_step[0].record(stream)
+    for i in range(args.steps):
         step.step()
-    e1.record(stream)
+        evs_step[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    step_ms = e0.elapsed_time(e1) / args.steps
+    step_ms = evs_step[0].elapsed_time(evs_step[-1]) / args.steps
+    per_step_us = [evs_step[i].elapsed_time(evs_step[i + 1]) * 1e3 for i in range(args.steps)]
 
     # ---- per-stage and per-launch timing (separate loops, same stream) ----
     def timed(fn, reps):
@@ -174,9 +176,22 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / reps
 
-    reps = max(5, args.steps // 2)
-    us_score = timed(step.score, reps)
-    us_select = timed(step.select, reps)
+    def timed_each(fn, reps):
+        """Per-repetition times (µs): an event between consecutive repetitions."""
+        es = [ev() for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        es[0].record(stream)
+        for i in range(reps):
+            fn()
+            es[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return [es[i].elapsed_time(es[i + 1]) * 1e3 for i in range(reps)]
+
+    reps = max(10, args.steps // 2)
+    t_score = timed_each(step.score, reps)
+    t_select = timed_each(step.select, reps)
+    us_score = float(np.mean(t_score))
+    us_select = float(np.mean(t_select))
     attn_layers = step.layers
     # every attention launch bracketed by its own events on the launch stream
     durs = []
@@ -189,9 +204,12 @@ def main():
         torch.cuda.synchronize()
         durs += [a.elapsed_time(b) * 1e3 for a, b in evs]
     us_attn_launch = float(np.mean(durs))
-    us_attn_all = timed(lambda: [step.attn(l) for l in attn_layers], reps)
+    t_attn_all = timed_each(lambda: [step.attn(l) for l in attn_layers], reps)
+    us_attn_all = float(np.mean(t_attn_all))
     dl = attn_layers[: max(1, min(args.dense_layers, len(attn_layers)))]
-    us_dense_layer = timed(lambda: [step.dense(l) for l in dl], 3) / len(dl)
+    t_dense_all = timed_each(lambda: [step.dense(l) for l in dl], 3)
+    us_dense_all = float(np.mean(t_dense_all))
+    us_dense_layer = us_dense_all / len(dl)
     # Vegas-style target signal on the same streams (raw logits summed over the first and
     # bonus queries, or over every query) and its pure top-k selection: not part of the step
     variants = {}
@@ -286,6 +304,14 @@ def main():
     b_step = b_score + b_select + len(attn_layers) * b_attn
     b_dense = attn_bytes(B, T.hq, T.hkv, T.d, nv, [n_ctx] * B) - B * n_ctx * 4   # no index list
     gbs = b_step / (step_ms * 1e-3) / 1e9
+    plan = D.dustin_attn_plan(B, T.hq, T.hkv, T.d, nv, inp.k_max, D.ATTN_LAYOUT_LIST)
+    # full-cache verification over every layer (the dense step: no scoring or selection)
+    us_dense_sum = us_dense_layer * len(attn_layers)
+
+    def spread(v):
+        q = np.percentile(np.asarray(v, dtype=np.float64), [10, 50, 90])
+        return {"p10": round(float(q[0]), 2), "median": round(float(q[1]), 2), "p90": round(float(q[2]), 2),
+                "n": len(v)}
     us_attn_call = us_attn_all / len(attn_layers)     # back-to-back calls, events around the loop
     attn_gbs = b_attn / (us_attn_call * 1e-6) / 1e9
 
@@ -310,6 +336,15 @@ def main():
         "stages_us": {"score_both_signals": round(us_score, 2), "select": round(us_select, 2),
                       "attn_per_call": round(us_attn_call, 2), "attn_per_call_own_events": round(us_attn_launch, 2),
                       "attn_all_layers": round(us_attn_all, 1)},
+        "stages_spread_us": {"step": spread(per_step_us), "score_both_signals": spread(t_score),
+                             "select": spread(t_select), "attn_all_layers": spread(t_attn_all),
+                             "attn_per_call_own_events": spread(durs),
+                             "dense_attn_all_layers": spread([t * len(attn_layers) / len(dl) for t in t_dense_all])},
+        "dense_step": {"sum_dense_attn_all_layers_us": round(us_dense_sum, 1), "layers": len(attn_layers),
+                       "layers_timed": len(dl),
+                       "step_speedup_sparse_vs_dense": round(us_dense_sum / (step_ms * 1e3), 3),
+                       "attn_speedup_sparse_vs_dense": round(us_dense_layer / us_attn_call, 3),
+                       "byte_ratio_dense_over_sparse_step": round(len(attn_layers) * b_dense / b_step, 3)},
         "bytes": {"step": b_step, "attn_per_launch": b_attn, "score": b_score, "select": b_select},
         "score_gbs": round(b_score / (us_score * 1e-6) / 1e9, 1),
         "dense_attn_per_layer_us": round(us_dense_layer, 2),
@@ -320,9 +355,8 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "dustin_sparse_verify_attn, one layer: verify_attn_split_kernel<128,3,2> "
-                               "+ verify_attn_merge_kernel<128,3,4>",
-                     "algorithmic_bytes_per_call": b_attn, "call_us": round(us_attn_call, 2)},
+                     "kernel": "dustin_sparse_verify_attn, one layer: " + D.attn_kernel_names(T.d, plan),
+                     "plan": plan, "algorithmic_bytes_per_call": b_attn, "call_us": round(us_attn_call, 2)},
     }
 
     if not args.no_cpu_baseline:
@@ -456,56 +490,145 @@ def estimator_sweep(dev, args):
                       "layer_extrapolation": "one layer of each model timed, times its layer count"}), flush=True)
 
 
-def cpu_baseline(inp, step, budget_s, b_attn, b_score, b_select, layers):
-    """The oracle (single-threaded C, fp64) on a bounded sample of the same workload:
-    sequence 0's scoring (both signals), selection and as many layers of its sparse
-    attention as fit the time budget.  Reported as algorithmic GB/s of that sample."""
+def _oracle_item(item):
+    """One shard of the oracle sample, run in a worker process: ("score", files, meta),
+    ("select", files, meta) or ("attn", files, meta).  Returns (kind, seconds of oracle
+    time).  Workers never touch the GPU: every input arrives as a .npy file."""
     import numpy as np
-    import torch
 
     from oracle import oracle as O
 
+    kind, files, meta = item
+    ld = lambda k: np.load(files[k])
+    if kind == "score":
+        acc = np.zeros((1, meta["n_max"]))
+        args = [(ld(f"K{i}"), ld(f"Q{i}"), meta["scale"][i]) for i in range(meta["n_groups"])]
+        ctx = ld("ctx")
+        t = time.perf_counter()
+        for K, Q, sc in args:
+            O.score_stream(K, Q, ctx, meta["n_max"], sc, O.PROB_SUM, acc)
+        return kind, time.perf_counter() - t
+    if kind == "select":
+        a = {k: ld(k) for k in ("ctx", "sd", "st", "budget", "n_sink", "n_window", "m")}
+        t = time.perf_counter()
+        O.select(a["ctx"], a["sd"], a["st"], a["budget"], a["n_sink"], a["n_window"], a["m"], meta["k_max"])
+        return kind, time.perf_counter() - t
+    Q, K, V, idx, cnt, ctx = (ld(k) for k in ("Q", "K", "V", "idx", "cnt", "ctx"))
+    t = time.perf_counter()
+    O.verify_attn(Q, K, V, ctx, idx, cnt, meta["scale"], meta["hkv"])
+    return kind, time.perf_counter() - t
+
+
+def _worker_ready(_):
+    from oracle import oracle as O
+    O.lib()
+    return os.getpid()
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(inp, step, budget_s, b_attn, b_score, b_select, layers):
+    """The oracle (plain C, fp64, single-threaded per process) on a bounded sample of the
+    same workload, sharded over the host's cores: every sequence's SRH scoring (both
+    signals) and selection, and the sparse attention of every sequence on as many layers
+    as the CPU-time budget allows (each (sequence, layer) an independent shard).  Shards
+    run in a pool of worker processes, one per core of the host's share (at most 16); the
+    figure is the sample's algorithmic bytes over the pool's wall time.  The same shards'
+    summed per-shard oracle times give the one-core figure beside it.  Attention shards get
+    the selected K/V rows and the new block compacted in list order with the list
+    renumbered 0..count-1: the oracle computes exactly the same sums over the same rows."""
+    import multiprocessing as mp
+    import shutil
+    import tempfile
+
+    import numpy as np
+    import torch
+
     u16 = lambda t: t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
     w = inp.w
-    B = w.batch
+    B, nv = w.batch, w.n_verify
     n = inp.n_max
-    ctx = inp.ctx_len.cpu().numpy()[:1]
-    secs = 0.0
-    for groups, q, caches, d in ((inp.draft_groups, inp.q_srh_draft, inp.draft_k, w.draft.d),
-                                 (inp.target_groups, inp.q_srh_target, inp.k_cache, w.target.d)):
-        acc = np.zeros((1, n))
-        qo = 0
-        for g in groups:
-            K = u16(caches[g.layer][:1, :n, g.kv_head])
-            Q = u16(q[:1, qo:qo + len(g.qheads)])
-            t = time.perf_counter()
-            O.score_stream(K, Q, ctx, n, 1.0 / math.sqrt(d), O.PROB_SUM, acc)
-            secs += time.perf_counter() - t
-            qo += len(g.qheads)
-    sd = step.score_draft[:1].double().cpu().numpy()
-    st = step.score_target[:1].double().cpu().numpy()
-    c = lambda x: x.cpu().numpy()[:1]
-    t = time.perf_counter()
-    idx, cnt = O.select(ctx, sd, st, c(inp.budget), c(inp.n_sink), c(inp.n_window), c(inp.m), inp.k_max)
-    secs += time.perf_counter() - t
-    nbytes = (b_score + b_select) / B
-    n_layers = 0
-    for l in layers:
-        rows = int(ctx[0]) + w.n_verify
-        K = u16(inp.k_cache[l][:1, :rows])
-        V = u16(inp.v_cache[l][:1, :rows])
-        Q = u16(inp.q_verify[l][:1])
-        t = time.perf_counter()
-        O.verify_attn(Q, K, V, ctx, idx, cnt, 1.0 / math.sqrt(w.target.d), w.target.hkv)
-        secs += time.perf_counter() - t
-        nbytes += b_attn / B
-        n_layers += 1
-        if secs >= budget_s:
-            break
-    return {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"sequence 0 of 8: SRH scoring (both signals), selection, sparse attention over "
-                      f"{n_layers} of {len(layers)} layers; {secs:.1f} s of oracle time",
-            "seconds": round(secs, 2), "host_cpus": os.cpu_count()}
+    ctx = inp.ctx_len.cpu().numpy().astype(np.int32)
+    cnt = step.count.cpu().numpy().astype(np.int32)
+    idx = step.idx.cpu().numpy()
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    P = max(1, min(16, cores))
+    # per-shard oracle seconds measured earlier on this workload: about 0.55 s of scoring per
+    # sequence and 0.09 s per (sequence, layer) of attention; the layer count fills the
+    # budget (10-30 s of single-core oracle time)
+    n_layers = max(1, min(len(layers), int(budget_s / (0.09 * B))))
+    shm = "/dev/shm" if os.path.isdir("/dev/shm") and shutil.disk_usage("/dev/shm").free > (4 << 30) else None
+    tmp = tempfile.mkdtemp(prefix="oracle_sample_", dir=shm)
+    items, nbytes = [], 0.0
+    try:
+        def save(name, arr):
+            path = os.path.join(tmp, name + ".npy")
+            np.save(path, np.ascontiguousarray(arr))
+            return path
+
+        sd = step.score_draft.double().cpu().numpy()
+        st = step.score_target.double().cpu().numpy()
+        for b in range(B):
+            files, scales, gi = {}, [], 0
+            for groups, q, caches, d in ((inp.draft_groups, inp.q_srh_draft, inp.draft_k, w.draft.d),
+                                         (inp.target_groups, inp.q_srh_target, inp.k_cache, w.target.d)):
+                qo = 0
+                for g in groups:
+                    files[f"K{gi}"] = save(f"s{b}_K{gi}", u16(caches[g.layer][b:b + 1, :n, g.kv_head]))
+                    files[f"Q{gi}"] = save(f"s{b}_Q{gi}", u16(q[b:b + 1, qo:qo + len(g.qheads)]))
+                    scales.append(1.0 / math.sqrt(d))
+                    qo += len(g.qheads)
+                    gi += 1
+            files["ctx"] = save(f"s{b}_ctx", ctx[b:b + 1])
+            items.append(("score", files, {"n_max": n, "scale": scales, "n_groups": gi}))
+            sel = {"ctx": ctx[b:b + 1], "sd": sd[b:b + 1], "st": st[b:b + 1]}
+            for k in ("budget", "n_sink", "n_window", "m"):
+                sel[k] = getattr(inp, k).cpu().numpy()[b:b + 1].astype(np.int32)
+            items.append(("select", {k: save(f"l{b}_{k}", v) for k, v in sel.items()}, {"k_max": inp.k_max}))
+            nbytes += (b_score + b_select) / B
+        for l in layers[:n_layers]:
+            for b in range(B):
+                c = int(cnt[b])
+                rows = torch.cat([step.idx[b, :c].long(),
+                                  torch.arange(int(ctx[b]), int(ctx[b]) + nv, device=step.idx.device)])
+                files = {"K": save(f"a{l}_{b}_K", u16(inp.k_cache[l][b].index_select(0, rows)[None])),
+                         "V": save(f"a{l}_{b}_V", u16(inp.v_cache[l][b].index_select(0, rows)[None])),
+                         "Q": save(f"a{l}_{b}_Q", u16(inp.q_verify[l][b:b + 1])),
+                         "idx": save(f"a{l}_{b}_idx", np.arange(c, dtype=np.int32)[None]),
+                         "cnt": save(f"a{l}_{b}_cnt", np.array([c], dtype=np.int32)),
+                         "ctx": save(f"a{l}_{b}_ctx", np.array([c], dtype=np.int32))}
+                items.append(("attn", files, {"scale": 1.0 / math.sqrt(w.target.d), "hkv": w.target.hkv}))
+                nbytes += b_attn / B
+        # the longest shards first, so the pool's tail is short
+        items.sort(key=lambda it: {"score": 0, "attn": 1, "select": 2}[it[0]])
+        ctx_mp = mp.get_context("spawn")
+        with ctx_mp.Pool(P) as pool:
+            pool.map(_worker_ready, range(P))          # interpreters and the oracle loaded
+            t0 = time.perf_counter()
+            res = pool.map(_oracle_item, items, chunksize=1)
+            wall = time.perf_counter() - t0
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    cpu_s = sum(r[1] for r in res)
+    return {"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": P, "kind": "oracle",
+            "sample": f"SRH scoring (both signals) and selection of all {B} sequences, sparse attention of all "
+                      f"{B} sequences on {n_layers} of {len(layers)} layers: {len(items)} independent shards in "
+                      f"a pool of {P} processes; {cpu_s:.1f} s of oracle time, {wall:.2f} s wall",
+            "cpu_model": cpu_model(), "host_cpus_visible": cores,
+            "single_core_gbs": round(nbytes / cpu_s / 1e9, 4), "wall_s": round(wall, 3),
+            "oracle_cpu_s": round(cpu_s, 2), "sample_bytes": int(nbytes)}
 
 
 if __name__ == "__main__":

@@ -194,6 +194,19 @@ dustin_status dustin_sparse_verify_attn(int B, int Hq, int Hkv, int head_dim, in
                                         void *out, float *lse, void *workspace,
                                         size_t workspace_bytes, void *stream);
 
+/* dustin_attn_plan — the launch plan the attention calls use for these sizes, for tools
+ * that name the kernels they time.  n_positions: k_max (sparse) or n_max (dense).
+ * layout: 0 = a sparse list, or paged views whose K and V rows sit at the same offsets;
+ * 1 = paged views with K and V rows at different offsets; 2 = dense over unpaged views.
+ *   plan (host int32 [5]): [0] 16-row query tiles per workgroup (the kernels' QT),
+ *   [1] query groups per (sequence, KV head), [2] splits of the position list,
+ *   [3] workgroups of the attention kernel, [4] how the splits are combined: 0 not at all
+ *   (one split), 1 by a second kernel, 2 inside the attention kernel
+ *   (DUSTIN_ATTN_FUSED_MERGE=1).  Errors as in the workspace-size queries.
+ */
+dustin_status dustin_attn_plan(int B, int Hq, int Hkv, int head_dim, int n_verify, int n_positions, int layout,
+                               int32_t *plan /* host */);
+
 /* dustin_sparse_verify_attn_noalloc — for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * dustin_sparse_verify_attn with the same arguments, results and errors, minus the

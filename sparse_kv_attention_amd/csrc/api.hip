@@ -515,6 +515,26 @@ dustin_status dense_verify_attn(int B, int Hq, int Hkv, int head_dim, int n_veri
                     scale, out, lse, workspace, workspace_bytes, stream);
 }
 
+dustin_status dustin_attn_plan(int B, int Hq, int Hkv, int head_dim, int n_verify, int n_positions, int layout,
+                               int32_t *plan)
+{
+    dustin_status st = DUSTIN_OK;
+    if (!plan || n_positions < 0 || layout < 0 || layout > 2)
+        return DUSTIN_ERR_INVALID_ARG;
+    if (!attn_shape_ok(B, Hq, Hkv, head_dim, n_verify, st))
+        return st;
+    if (n_positions + n_verify > kMaxList)
+        return DUSTIN_ERR_UNSUPPORTED;
+    const AttnWs lay = attn_workspace(B, Hq, Hkv, head_dim, n_verify, n_positions + n_verify,
+                                      attn_split_cap(layout != 2, layout == 1));
+    plan[0] = lay.plan.qt;
+    plan[1] = lay.plan.qgroups;
+    plan[2] = lay.plan.splits;
+    plan[3] = (int32_t)lay.plan.grid;
+    plan[4] = lay.plan.splits == 1 ? 0 : (env_flag("DUSTIN_ATTN_FUSED_MERGE", false) ? 2 : 1);
+    return DUSTIN_OK;
+}
+
 dustin_status dustin_kv_write_block(int B, int Hkv, int head_dim, int n_new, const void *k_new,
                                     const void *v_new, const int32_t *ctx_len, const dustin_kv_view *k,
                                     const dustin_kv_view *v, void *stream)

@@ -72,6 +72,7 @@ _sparse = _decl("dustin_sparse_verify_attn", [_I, _I, _I, _I, _I, _P, ctypes.POI
 _sparse_noalloc = _decl("dustin_sparse_verify_attn_noalloc",
                          [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView), ctypes.POINTER(KvView), _P, _P, _P,
                           _I, _F, _P, _P, _P])
+_attn_plan = _decl("dustin_attn_plan", [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_int32)])
 _dense_ws = _decl("dense_verify_attn_workspace_size", [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)])
 _dense = _decl("dense_verify_attn", [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView),
                                      ctypes.POINTER(KvView), _P, _I, _F, _P, _P, _P, _SZ, _P])
@@ -83,7 +84,7 @@ _recovery = _decl("dustin_attn_recovery", [_I, _P, _P, _P, _P])
 EXPORTED = ("dustin_status_string", "dustin_srh_score_workspace_size", "dustin_srh_score",
             "dustin_select_workspace_size", "dustin_select",
             "dustin_sparse_verify_attn_workspace_size", "dustin_sparse_verify_attn",
-            "dustin_sparse_verify_attn_noalloc",
+            "dustin_sparse_verify_attn_noalloc", "dustin_attn_plan",
             "dense_verify_attn_workspace_size", "dense_verify_attn",
             "dustin_kv_write_block", "dustin_kv_commit", "dustin_attn_recovery")
 
@@ -212,6 +213,26 @@ def dense_verify_attn_workspace_size(B, Hq, Hkv, head_dim, n_verify, n_max) -> i
     n = _SZ(0)
     _check(_dense_ws(B, Hq, Hkv, head_dim, n_verify, n_max, ctypes.byref(n)), "dense_verify_attn_workspace_size")
     return n.value
+
+
+ATTN_LAYOUT_LIST, ATTN_LAYOUT_TWO_TABLES, ATTN_LAYOUT_DENSE = 0, 1, 2
+
+
+def dustin_attn_plan(B, Hq, Hkv, head_dim, n_verify, n_positions, layout=ATTN_LAYOUT_LIST) -> dict:
+    """The attention launch plan for these sizes: query tiles per workgroup, query groups,
+    splits, workgroups and how the splits are combined ("none", "merge kernel", "fused")."""
+    p = (ctypes.c_int32 * 5)()
+    _check(_attn_plan(B, Hq, Hkv, head_dim, n_verify, n_positions, layout, p), "dustin_attn_plan")
+    return {"qt": p[0], "qgroups": p[1], "splits": p[2], "workgroups": p[3],
+            "merge": ("none", "merge kernel", "fused")[p[4]]}
+
+
+def attn_kernel_names(head_dim, plan: dict) -> str:
+    """The kernels one attention call launches under `plan`."""
+    names = f"verify_attn_kernel<{head_dim}, {plan['qt']}>"
+    if plan["merge"] == "merge kernel":
+        names += f" + verify_attn_merge_kernel<{head_dim}, {plan['qt']}>"
+    return names
 
 
 def _attn_common(q, out, lse):

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(D.EXPORTED)
     out = subprocess.run(["nm", "-D", "--defined-only", D.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -118,6 +118,26 @@ def test_noalloc_attn_rejects_on_the_host():
                        (dict(k=view(stride_token=1001)), D.ERR_INVALID_ARG), (dict(out=None), D.ERR_INVALID_ARG)]:
         assert noalloc(**kw) == status, kw
     assert noalloc(B=0, q=None, out=None) == D.OK
+
+
+def test_attn_plan_query():
+    """The plan query: 8 sequences x 8 KV heads with 40 query rows (64 q-heads, 5 queries)
+    and a 2048-position list: 3 query tiles, one query group, four splits over 256 workgroups
+    on a 256-CU plan, combined by the merge kernel."""
+    import os as _os
+    old = _os.environ.pop("DUSTIN_ATTN_TARGET_WGS", None)
+    _os.environ["DUSTIN_ATTN_TARGET_WGS"] = "256"
+    try:
+        p = D.dustin_attn_plan(8, 64, 8, 128, 5, 2048)
+        assert p == {"qt": 3, "qgroups": 1, "splits": 4, "workgroups": 256, "merge": "merge kernel"}, p
+        assert D.attn_kernel_names(128, p) == "verify_attn_kernel<128, 3> + verify_attn_merge_kernel<128, 3>"
+        assert D.dustin_attn_plan(64, 64, 8, 128, 5, 1024)["merge"] == "none"
+        with pytest.raises(D.DustinError):
+            D.dustin_attn_plan(8, 64, 8, 128, 5, 2048, layout=3)
+    finally:
+        _os.environ.pop("DUSTIN_ATTN_TARGET_WGS", None)
+        if old is not None:
+            _os.environ["DUSTIN_ATTN_TARGET_WGS"] = old
 
 
 def test_dense_rejects():
