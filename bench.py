@@ -206,6 +206,11 @@ def main():
     us_attn_launch = float(np.mean(durs))
     t_attn_all = timed_each(lambda: [step.attn(l) for l in attn_layers], reps)
     us_attn_all = float(np.mean(t_attn_all))
+    # the same calls also writing the Collect-2 logit sums of the selected tokens (every KV
+    # head of every layer) as a by-product of verification
+    lg2 = torch.empty((B, T.hkv, inp.k_max), dtype=torch.float32, device=dev)
+    t_attn_lg = timed_each(lambda: [step.attn_logits(l, lg2) for l in attn_layers], reps)
+    us_attn_lg = float(np.mean(t_attn_lg)) / len(attn_layers)
     dl = attn_layers[: max(1, min(args.dense_layers, len(attn_layers)))]
     t_dense_all = timed_each(lambda: [step.dense(l) for l in dl], 3)
     us_dense_all = float(np.mean(t_dense_all))
@@ -290,6 +295,9 @@ def main():
         "kv_write_block_us": round(us_write, 2),
         "kv_write_block_bytes": 2 * 2 * B * nv * T.hkv * T.d * 2,
         "kv_commit_us": round(us_commit, 2),
+        "attn_with_collect2_logits_per_call_us": round(us_attn_lg, 2),
+        "collect2_logits_added_per_call_us": round(us_attn_lg - us_attn_all / len(attn_layers), 2),
+        "collect2_logits_bytes_per_call": B * T.hkv * sum(int(c) for c in counts) * 4,
         "sparse_decode_nv1_per_call_us": round(us_decode, 2),
         "sparse_decode_nv1_gbs": round(b_decode / (us_decode * 1e-6) / 1e9, 1),
         "attn_recovery": recovery,

@@ -194,6 +194,27 @@ dustin_status dustin_sparse_verify_attn(int B, int Hq, int Hkv, int head_dim, in
                                         void *out, float *lse, void *workspace,
                                         size_t workspace_bytes, void *stream);
 
+/* dustin_sparse_verify_attn_logits — dustin_sparse_verify_attn that also writes the
+ * Collect-2 signal of the selected tokens as a by-product of verification (German Vegas
+ * summary, 2B "Collect-2-Query" and 3 "Kernel-Instrumentierung": the verification kernel
+ * itself hands out the pre-softmax logits of the first and the bonus verify query):
+ *   logit_sum2[b][g][j] = sum over the query heads h of KV head g and t in {0, n_verify-1}
+ *                         (t = 0 once when n_verify == 1) of scale * q[b][t][h] . K[b][i][g]
+ *   for list entries j < count[b] (clamped as in the attention), i = idx[b][j] (clamped);
+ *   entries j >= count[b] are not written.
+ *   logit_sum2 : fp32 [B][Hkv][k_max], 4-byte aligned (else INVALID_ARG).
+ * The other arguments, results and errors are those of dustin_sparse_verify_attn, with
+ * the same workspace; a shape whose query rows per KV head (Hq/Hkv * n_verify) exceed 80
+ * returns DUSTIN_ERR_UNSUPPORTED (each (sequence, KV head) must fit one workgroup).
+ */
+dustin_status dustin_sparse_verify_attn_logits(int B, int Hq, int Hkv, int head_dim, int n_verify,
+                                               const void *q, const dustin_kv_view *k /* host */,
+                                               const dustin_kv_view *v /* host */,
+                                               const int32_t *ctx_len, const int32_t *idx,
+                                               const int32_t *count, int k_max, float scale,
+                                               void *out, float *lse, float *logit_sum2,
+                                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* dustin_attn_plan — the launch plan the attention calls use for these sizes, for tools
  * that name the kernels they time.  n_positions: k_max (sparse) or n_max (dense).
  * layout: 0 = a sparse list, or paged views whose K and V rows sit at the same offsets;

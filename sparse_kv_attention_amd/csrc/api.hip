@@ -198,7 +198,7 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
                        const dustin_kv_view *k, const dustin_kv_view *v, const int32_t *ctx_len,
                        const int32_t *idx, const int32_t *count, int k_max, int n_max,
                        float scale, void *out, float *lse, void *ws, size_t ws_bytes, void *stream,
-                       bool use_scratch = false)
+                       bool use_scratch = false, float *logit2 = nullptr)
 {
     dustin_status st = DUSTIN_OK;
     if (!attn_shape_ok(B, Hq, Hkv, head_dim, n_verify, st))
@@ -227,6 +227,9 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
         return DUSTIN_ERR_UNSUPPORTED;
     const AttnWs lay = attn_workspace(B, Hq, Hkv, head_dim, n_verify, max_list,
                                       attn_split_cap(sparse || rows_mode, rows_mode && !kv_same));
+    // the Collect-2 emission needs every query row of a (sequence, KV head) in one workgroup
+    if (logit2 && lay.plan.qgroups != 1)
+        return DUSTIN_ERR_UNSUPPORTED;
     if (use_scratch) {
         // every host check has passed: only now the scratch of the current device
         if (lay.bytes > DUSTIN_NOALLOC_SCRATCH_BYTES)
@@ -262,6 +265,8 @@ dustin_status run_attn(int B, int Hq, int Hkv, int head_dim, int n_verify, const
     a.counter = reinterpret_cast<unsigned long long *>(static_cast<char *>(ws) + lay.ctr_off);
     a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + lay.part_off);
     a.fused_merge = env_flag("DUSTIN_ATTN_FUSED_MERGE", false) ? 1 : 0;
+    a.logit2 = logit2;
+    a.scale = scale;
     a.splits = lay.plan.splits;
     a.spl = lay.plan.spl;
     a.qgroups = lay.plan.qgroups;
@@ -490,6 +495,19 @@ dustin_status dustin_sparse_verify_attn_noalloc(int B, int Hq, int Hkv, int head
         return DUSTIN_ERR_INVALID_ARG;
     return run_attn(B, Hq, Hkv, head_dim, n_verify, q, k, v, ctx_len, idx, count, k_max, 0, scale,
                     out, lse, nullptr, 0, stream, true);
+}
+
+dustin_status dustin_sparse_verify_attn_logits(int B, int Hq, int Hkv, int head_dim, int n_verify,
+                                               const void *q, const dustin_kv_view *k,
+                                               const dustin_kv_view *v, const int32_t *ctx_len,
+                                               const int32_t *idx, const int32_t *count, int k_max,
+                                               float scale, void *out, float *lse, float *logit_sum2,
+                                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!idx || !count || !logit_sum2 || (reinterpret_cast<uintptr_t>(logit_sum2) & 3u))
+        return DUSTIN_ERR_INVALID_ARG;
+    return run_attn(B, Hq, Hkv, head_dim, n_verify, q, k, v, ctx_len, idx, count, k_max, 0, scale,
+                    out, lse, workspace, workspace_bytes, stream, false, logit_sum2);
 }
 
 dustin_status dense_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_dim, int n_verify,

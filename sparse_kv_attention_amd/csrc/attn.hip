@@ -66,6 +66,31 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
 }
 
 // max over the four lanes l, l^16, l^32, l^48 (v_permlane32_swap / v_permlane16_swap)
+// In-place sum over each 16-lane row of N values per lane (quad_perm xor 1 and xor 2,
+// row_half_mirror, row_mirror); every lane of a row ends with its row's sums.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+template <int N>
+__device__ __forceinline__ void row16_sum(float (&v)[N])
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] += dpp_f32<0xB1>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] += dpp_f32<0x4E>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] += dpp_f32<0x141>(v[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] += dpp_f32<0x140>(v[i]);
+}
+
 __device__ __forceinline__ float max_over_quads(float x)
 {
     const uint32_t u = __float_as_uint(x);
@@ -247,7 +272,8 @@ __device__ __forceinline__ void split_write(const AttnArgs &a, const SplitSum &t
         a.lse[((int64_t)b * a.Hq + h) * a.nv + tq] = lse;
 }
 
-template <int D, int QT>
+// EMIT: also write the Collect-2 logit sums of the list rows (a.logit2)
+template <int D, int QT, bool EMIT>
 __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
 {
     using S = AttnShape<D, QT>;
@@ -310,6 +336,16 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
             __builtin_amdgcn_global_load_lds((const void *)(a.q + ((int64_t)(b * a.nv + t) * a.Hq + h) * D + ck * 8),
                                              (lds_void *)(lds + n * 1024), 16, 0, 0);
         }
+    }
+    // Collect-2 emission (one query group holds every row of the pair): lane column li of
+    // tile qt counts when its query row is a real row of verify query 0 or n_verify-1
+    constexpr bool emit = EMIT;
+    float wq[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        const int row = qt * 16 + li;
+        const int t = row / a.G;
+        wq[qt] = emit && row < a.GV && (t == 0 || t == a.nv - 1) ? 1.f : 0.f;
     }
     int qrow_t[QT];   // verify index t of the lane's query row (large for padding rows)
 #pragma unroll
@@ -518,6 +554,35 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
                 for (int ks = 0; ks < G::KS; ++ks)
                     s[h][qt] = mfma_bf16(kop[h][ks], qop[qt][ks], s[h][qt]);
             }
+
+        // Collect-2 logits of the step's list rows: the emitted columns summed per row
+        // (over the tiles, then over the 16 lanes of the row's quad), scaled to natural-log
+        // units; lane 0 of each quad stores its 8 rows
+        if (emit && !direct) {
+            float e[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int qt = 0; qt < QT; ++qt)
+                        v += wq[qt] * s[h][qt][r];
+                    e[4 * h + r] = v;
+                }
+            row16_sum<8>(e);
+            if (li == 0) {
+                float *dst = a.logit2 + ((int64_t)b * a.Hkv + g) * a.k_max;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int pos = pos0 + trow[h][r];
+                        if (pos < pend)
+                            dst[pos] = e[4 * h + r] * a.scale;
+                    }
+            }
+        }
 
         u32x4 pb[QT];
 #pragma unroll
@@ -920,7 +985,10 @@ __global__ __launch_bounds__(kThreads) void verify_attn_merge_kernel(AttnArgs a)
 template <int D, int QT>
 hipError_t launch_qt(const AttnArgs &a, dim3 grid, hipStream_t st)
 {
-    hipLaunchKernelGGL((verify_attn_kernel<D, QT>), grid, dim3(kThreads), 0, st, a);
+    if (a.logit2)
+        hipLaunchKernelGGL((verify_attn_kernel<D, QT, true>), grid, dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((verify_attn_kernel<D, QT, false>), grid, dim3(kThreads), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1 || a.fused_merge)
         return e;

@@ -36,6 +36,9 @@ struct AttnArgs {
     float *part;             // split partials
     unsigned long long *counter;   // per pair: arrivals of its splits (fused merge)
     int fused_merge;         // splits merged by their last arrival (else by a second kernel)
+    float *logit2;           // optional [B][Hkv][k_max]: per selected token, scale * q.k summed over
+                             //   the KV head's query heads and verify queries {0, n_verify-1}
+    float scale;             // softmax scale (natural-log logits of logit2)
     int splits, spl, qgroups, pairs;   // spl: list positions per split; pairs = B*Hkv*qgroups
 };
 

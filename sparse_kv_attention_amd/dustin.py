@@ -72,6 +72,9 @@ _sparse = _decl("dustin_sparse_verify_attn", [_I, _I, _I, _I, _I, _P, ctypes.POI
 _sparse_noalloc = _decl("dustin_sparse_verify_attn_noalloc",
                          [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView), ctypes.POINTER(KvView), _P, _P, _P,
                           _I, _F, _P, _P, _P])
+_sparse_logits = _decl("dustin_sparse_verify_attn_logits",
+                        [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView), ctypes.POINTER(KvView), _P, _P, _P, _I,
+                         _F, _P, _P, _P, _P, _SZ, _P])
 _attn_plan = _decl("dustin_attn_plan", [_I, _I, _I, _I, _I, _I, _I, ctypes.POINTER(ctypes.c_int32)])
 _dense_ws = _decl("dense_verify_attn_workspace_size", [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)])
 _dense = _decl("dense_verify_attn", [_I, _I, _I, _I, _I, _P, ctypes.POINTER(KvView),
@@ -84,7 +87,7 @@ _recovery = _decl("dustin_attn_recovery", [_I, _P, _P, _P, _P])
 EXPORTED = ("dustin_status_string", "dustin_srh_score_workspace_size", "dustin_srh_score",
             "dustin_select_workspace_size", "dustin_select",
             "dustin_sparse_verify_attn_workspace_size", "dustin_sparse_verify_attn",
-            "dustin_sparse_verify_attn_noalloc", "dustin_attn_plan",
+            "dustin_sparse_verify_attn_noalloc", "dustin_attn_plan", "dustin_sparse_verify_attn_logits",
             "dense_verify_attn_workspace_size", "dense_verify_attn",
             "dustin_kv_write_block", "dustin_kv_commit", "dustin_attn_recovery")
 
@@ -253,6 +256,21 @@ def dustin_sparse_verify_attn(q, k: KvView, v: KvView, Hkv: int, ctx_len, idx, c
     _check(_sparse(B, Hq, Hkv, d, nv, _ptr(q), ctypes.byref(k), ctypes.byref(v), _ptr(ctx_len), _ptr(idx),
                    _ptr(count), idx.shape[1], float(scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
                    _stream(stream)), "dustin_sparse_verify_attn")
+
+
+def dustin_sparse_verify_attn_logits(q, k: KvView, v: KvView, Hkv: int, ctx_len, idx, count, scale: float,
+                                     out, lse, logit_sum2, ws, stream=None):
+    """dustin_sparse_verify_attn that also writes, per selected token, the Collect-2 logit
+    sum (queries 0 and n_verify-1, summed over the KV head's query heads) into
+    logit_sum2 fp32 [B][Hkv][k_max]."""
+    B, nv, Hq, d = _attn_common(q, out, lse)
+    _dev_i32(ctx_len, "ctx_len"); _dev_i32(idx, "idx"); _dev_i32(count, "count")
+    if (logit_sum2.dtype != torch.float32 or not logit_sum2.is_contiguous()
+            or tuple(logit_sum2.shape) != (B, Hkv, idx.shape[1])):
+        raise ValueError("logit_sum2 must be contiguous fp32 [B][Hkv][k_max]")
+    _check(_sparse_logits(B, Hq, Hkv, d, nv, _ptr(q), ctypes.byref(k), ctypes.byref(v), _ptr(ctx_len), _ptr(idx),
+                          _ptr(count), idx.shape[1], float(scale), _ptr(out), _ptr(lse), _ptr(logit_sum2), _ptr(ws),
+                          ws.numel(), _stream(stream)), "dustin_sparse_verify_attn_logits")
 
 
 def dustin_sparse_verify_attn_noalloc(q, k: KvView, v: KvView, Hkv: int, ctx_len, idx, count, scale: float,

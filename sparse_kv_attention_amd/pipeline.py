@@ -91,6 +91,14 @@ class SparseVerifyStep:
                                     self.count, self.scale, self.out if out is None else out,
                                     self.lse if lse is None else lse, self.ws_attn, stream)
 
+    def attn_logits(self, layer: int, logit_sum2, out=None, lse=None, stream=None):
+        """attn() that also writes the Collect-2 logit sums of the selected tokens
+        (fp32 [B][Hkv][k_max]) as a by-product of verification."""
+        k, v = self.kv[layer]
+        D.dustin_sparse_verify_attn_logits(self.inp.q_verify[layer], k, v, self.T.hkv, self.inp.ctx_len, self.idx,
+                                           self.count, self.scale, self.out if out is None else out,
+                                           self.lse if lse is None else lse, logit_sum2, self.ws_attn, stream)
+
     def dense(self, layer: int, out=None, lse=None, stream=None):
         k, v = self.kv[layer]
         D.dense_verify_attn(self.inp.q_verify[layer], k, v, self.T.hkv, self.inp.ctx_len, self.n_max,

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert set(names) == set(D.EXPORTED)
     out = subprocess.run(["nm", "-D", "--defined-only", D.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -118,6 +118,17 @@ def test_noalloc_attn_rejects_on_the_host():
                        (dict(k=view(stride_token=1001)), D.ERR_INVALID_ARG), (dict(out=None), D.ERR_INVALID_ARG)]:
         assert noalloc(**kw) == status, kw
     assert noalloc(B=0, q=None, out=None) == D.OK
+
+
+def test_collect2_logits_call_rejects_on_the_host():
+    k = view(n_tokens=8192)
+    f = lambda **kw: D._sparse_logits(kw.get("B", 2), kw.get("Hq", 64), 8, 128, kw.get("nv", 5), FAKE, ctypes.byref(k),
+                                      ctypes.byref(k), FAKE, FAKE, FAKE, 256, 0.1, FAKE, FAKE, kw.get("lg", FAKE),
+                                      FAKE, 1 << 30, None)
+    assert f(lg=None) == D.ERR_INVALID_ARG
+    assert f(lg=FAKE + 2) == D.ERR_INVALID_ARG
+    assert f(nv=11) == D.ERR_UNSUPPORTED          # 8 query heads x 11 queries: two query groups
+    assert f(B=0) == D.OK
 
 
 def test_attn_plan_query():

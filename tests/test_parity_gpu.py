@@ -4,14 +4,15 @@ Bars: scores within 1e-5 relative (+1e-10 absolute floor; for logit sums the rel
 term is taken against the sum of |logits|), selection bit-exact when the oracle selects
 on the GPU's own fp32 scores, attention output max-abs 2e-2 and LSE 1e-3.
 """
+import math
 import os
 
 import numpy as np
 import pytest
 import torch
 
-from _harness import (check_attn, check_scores, logit_abs_sum, oracle_attn, oracle_scores,
-                      oracle_select_on, say)
+from _harness import (SCORE_ATOL, SCORE_RTOL, check_attn, check_scores, logit_abs_sum, oracle_attn,
+                      oracle_scores, oracle_select_on, rows, say, u16)
 from oracle import oracle as O
 from sparse_kv_attention_amd import workloads as W
 from sparse_kv_attention_amd.workloads import ModelShape, Workload
@@ -316,6 +317,75 @@ def test_fused_split_merge_matches_merge_kernel_bitwise():
                 for o, l in fused + two[1:]:
                     assert torch.equal(o, two[0][0]) and torch.equal(l, two[0][1]), what
                 check_attn(fused[0][0], fused[0][1], refd if dense else ref, bs, what)
+
+
+def _collect2_reference(inp, layer, idx, cnt, bsel):
+    """Oracle LOGIT_SUM2 over each KV head's query heads at the listed positions, and the
+    sum of |logits| of the same terms (the conditioning of the sum)."""
+    w = inp.w
+    T = w.target
+    G = T.hq // T.hkv
+    nv = w.n_verify
+    scale = 1.0 / math.sqrt(T.d)
+    ctx = inp.ctx_len.cpu().numpy()
+    ref = {}
+    for i, b in enumerate(bsel):
+        K = rows(inp, inp.k_cache[layer], b, inp.n_max).cpu()                 # [n_max][Hkv][d]
+        for g in range(T.hkv):
+            Q = inp.q_verify[layer][b:b + 1, :, g * G:(g + 1) * G].permute(0, 2, 1, 3).contiguous().cpu()
+            acc = O.score_stream(u16(K[None, :, g]), u16(Q), ctx[b:b + 1], inp.n_max, scale, O.LOGIT_SUM2)
+            js = sorted({0, nv - 1})
+            cond = (K[:, g].double() @ Q[0][:, js].double().reshape(-1, T.d).T).abs().sum(1).numpy() * scale
+            c = int(cnt[b])
+            ref[(b, g)] = (acc[0][idx[b, :c]], cond[idx[b, :c]])
+    return ref
+
+
+@pytest.mark.parametrize("case", ["qwen7b", "paged_two_tables", "single_query", "d64_odd_group"])
+def test_collect2_logits_emitted_by_verification(case):
+    """The verification kernel's Collect-2 by-product: per selected token, the scaled
+    pre-softmax logits of verify queries 0 and n_verify-1 summed over the KV head's query
+    heads, against the oracle's LOGIT_SUM2 at the listed positions (1e-5 of the sum of
+    |logits|); the attention output is unchanged bit for bit by the emission."""
+    from sparse_kv_attention_amd import dustin as D
+    if case == "qwen7b":
+        w = W.shrink(W.QWEN7B, target=ModelShape(2, 28, 4, 128), srh_target=((0, 0), (1, 0)))
+    elif case == "single_query":
+        w = small("c2_nv1", 2, 900, 16, 2, 128, 0, 200, 4, 16, 40, seed=41)
+    elif case == "d64_odd_group":
+        w = small("c2_d64", 3, 1200, 14, 2, 64, 6, 300, 4, 32, 60, seed=42)
+    else:
+        w = small("c2_paged", 3, 1500, 16, 2, 128, 4, 400, 4, 32, 100, seed=43)
+    inp = W.make_inputs(w, device="cuda")
+    step = step_for(inp, [0])
+    step.score()
+    step.select()
+    if case == "paged_two_tables":
+        K, V = inp.k_cache[0], inp.v_cache[0]
+        kp, ptk = _paged_copy(K, 16, 5)
+        vp, ptv = _paged_copy(V, 16, 6)
+        step.kv[0] = (D.kv_view(kp, ptk), D.kv_view(vp, ptv))
+    B = w.batch
+    lg = torch.full((B, w.target.hkv, inp.k_max), float("nan"), dtype=torch.float32, device="cuda")
+    step.attn(0)
+    torch.cuda.synchronize()
+    out0, lse0 = step.out.clone(), step.lse.clone()
+    step.attn_logits(0, lg)
+    torch.cuda.synchronize()
+    assert torch.equal(step.out, out0) and torch.equal(step.lse, lse0), "the emission changed the attention"
+    idx, cnt = step.idx.cpu().numpy(), step.count.cpu().numpy()
+    bs = list(range(B))
+    ref = _collect2_reference(inp, 0, idx, cnt, bs)
+    got = lg.cpu().numpy()
+    worst = 0.0
+    for (b, g), (r, cond) in ref.items():
+        c = int(cnt[b])
+        e = np.abs(got[b, g, :c].astype(np.float64) - r)
+        tol = SCORE_RTOL * cond + SCORE_ATOL
+        assert np.all(e <= tol), (case, b, g, float(np.max(e / tol)))
+        assert np.all(np.isnan(got[b, g, c:])), "entries past the count were written"
+        worst = max(worst, float(np.max(e / tol)) if c else 0.0)
+    say(f"  collect-2 logits ({case}): max err/tol = {worst:.3g} over {int(cnt.sum())} tokens x {w.target.hkv} heads")
 
 
 def test_step_replayed_as_hip_graph_matches_eager():
