@@ -484,11 +484,25 @@ def estimator_sweep(dev, args):
         us_srh = timed(step.score, reps)
         naive = T.layers * us_t + Dm.layers * us_d
         dense = T.layers * us_dense
+        # bytes of one layer's naive estimate: every K row of every KV head once (the
+        # method's minimum), and as launched (each group of <= 16 (head, query) pairs reads
+        # its KV head's rows again)
+        kb_t = w.batch * n * T.hkv * T.d * 2
+        kb_d = w.batch * n * Dm.hkv * Dm.d * 2
+        rd_t = sum(len(g) for g, _ in est_t.calls) * w.batch * n * T.d * 2
+        rd_d = sum(len(g) for g, _ in est_d.calls) * w.batch * n * Dm.d * 2
+        b_dense = attn_bytes(w.batch, T.hq, T.hkv, T.d, w.n_verify, [n] * w.batch) - w.batch * n * 4
         points.append({"ctx": n, "naive_target_layer_us": round(us_t, 2), "naive_draft_layer_us": round(us_d, 2),
                        "dense_layer_us": round(us_dense, 2), "naive_all_layers_us": round(naive, 1),
                        "dense_all_layers_us": round(dense, 1), "srh_scoring_us": round(us_srh, 2),
                        "naive_over_dense": round(naive / dense, 3), "srh_over_dense": round(us_srh / dense, 5),
-                       "naive_calls_per_layer": {"target": len(est_t.calls), "draft": len(est_d.calls)}})
+                       "naive_calls_per_layer": {"target": len(est_t.calls), "draft": len(est_d.calls)},
+                       "naive_target_layer_bytes": kb_t, "naive_target_layer_bytes_as_launched": rd_t,
+                       "naive_draft_layer_bytes": kb_d, "naive_draft_layer_bytes_as_launched": rd_d,
+                       "naive_all_layers_bytes": T.layers * kb_t + Dm.layers * kb_d,
+                       "dense_all_layers_bytes": T.layers * b_dense,
+                       "naive_target_gbs_as_launched": round(rd_t / (us_t * 1e-6) / 1e9, 1),
+                       "dense_gbs": round(b_dense / (us_dense * 1e-6) / 1e9, 1)})
         print(f"# ctx {n}: {points[-1]}", file=sys.stderr, flush=True)
         del step, est_t, est_d, inp
         torch.cuda.empty_cache()
