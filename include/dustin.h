@@ -136,6 +136,33 @@ dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_g
                                const void *q, int n_q, float scale, int mode, float *score,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* Both signals in one call (the draft lookahead and the target historical queries score
+ * the same contexts): the softmax-mode signals share one logit launch and every signal one
+ * finalize launch, so the launch ramp and tail are paid once.  Each signal's results are
+ * those of a dustin_srh_score call with its own arguments, up to the rounding order of the
+ * per-workgroup statistics (the grid is shared, so a stream's tiles fall into different
+ * workgroup shares); every argument rule of dustin_srh_score applies per signal.
+ *   signals   : (host) [n_signals], 1 <= n_signals <= 2; at most 16 groups in all
+ *   workspace : dustin_srh_score_signals_workspace_size(...) bytes, 16-byte aligned
+ */
+typedef struct {
+    int32_t n_groups;
+    const dustin_srh_group *groups; /* host [n_groups]                                   */
+    int32_t head_dim;               /* 64 or 128, shared by the signal's groups           */
+    const void *q;                  /* bf16 [B][sum of n_qheads][n_q][head_dim]           */
+    int32_t n_q;
+    float scale;
+    int32_t mode;                   /* DUSTIN_SCORE_*                                     */
+    float *score;                   /* fp32 [B][n_max], fully written                     */
+} dustin_srh_signal;
+
+dustin_status dustin_srh_score_signals_workspace_size(int B, int n_max, int n_signals,
+                                                      const dustin_srh_signal *signals /* host */,
+                                                      size_t *bytes /* host */);
+dustin_status dustin_srh_score_signals(int B, int n_max, const int32_t *ctx_len, int n_signals,
+                                       const dustin_srh_signal *signals /* host */, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------------------------
  * Step 3 — hybrid budgeted selection of I_verify.
  * Per sequence b, with N = ctx_len[b] clamped to [0, n_max] and

@@ -336,75 +336,168 @@ dustin_status dustin_srh_score_workspace_size(int B, int n_max, int total_qheads
     return DUSTIN_OK;
 }
 
-dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_groups,
-                               const dustin_srh_group *groups, int head_dim, const void *q, int n_q,
-                               float scale, int mode, float *score, void *workspace,
-                               size_t workspace_bytes, void *stream)
+namespace {
+
+// Host checks of one signal: sizes, mode, groups; its query heads and widest group.
+dustin_status check_signal(const dustin_srh_signal &sg, int &total_qheads, int &max_pairs, int &ctx_clamp, int n_max)
 {
-    if (B < 0 || n_max < 0 || n_q <= 0 || !std::isfinite(scale))
+    if (sg.n_q <= 0 || !std::isfinite(sg.scale) || !score_mode_ok(sg.mode) || sg.n_groups < 1 || !sg.groups)
         return DUSTIN_ERR_INVALID_ARG;
-    if (!score_mode_ok(mode))
-        return DUSTIN_ERR_INVALID_ARG;
-    if (n_groups < 1 || !groups)
-        return DUSTIN_ERR_INVALID_ARG;
-    if (n_groups > kMaxGroups || (head_dim != 64 && head_dim != 128) || n_q > 16)
+    if (sg.n_groups > kMaxGroups || (sg.head_dim != 64 && sg.head_dim != 128) || sg.n_q > 16)
         return DUSTIN_ERR_UNSUPPORTED;
-    if (B == 0 || n_max == 0)
-        return DUSTIN_OK;
-    if (!ctx_len || !q || !score || !aligned16(q) || !aligned16(score))
-        return DUSTIN_ERR_INVALID_ARG;
-    const int ppq = pairs_per_qhead(n_q, mode);
-    int total_qheads = 0, max_pairs = 0, ctx_clamp = n_max;
-    for (int i = 0; i < n_groups; ++i) {
-        const dustin_srh_group &g = groups[i];
+    const int ppq = pairs_per_qhead(sg.n_q, sg.mode);
+    total_qheads = 0;
+    max_pairs = 0;
+    ctx_clamp = n_max;
+    for (int i = 0; i < sg.n_groups; ++i) {
+        const dustin_srh_group &g = sg.groups[i];
         if (g.n_qheads <= 0 || g.kv_head < 0 || !view_ok(&g.k, g.kv_head + 1, 1))
             return DUSTIN_ERR_INVALID_ARG;
-        if (g.n_qheads * ppq > (mode == DUSTIN_SCORE_PROB_SUM ? kMaxProbPairsPerGroup : kMaxPairsPerGroup))
+        if (g.n_qheads * ppq > (sg.mode == DUSTIN_SCORE_PROB_SUM ? kMaxProbPairsPerGroup : kMaxPairsPerGroup))
             return DUSTIN_ERR_UNSUPPORTED;
         total_qheads += g.n_qheads;
         max_pairs = std::max(max_pairs, g.n_qheads * ppq);
         ctx_clamp = std::min(ctx_clamp, view_cap(&g.k));
     }
-    const ScoreWs lay = score_workspace(B, n_max, total_qheads, n_q, mode);
-    if (!workspace || workspace_bytes < lay.bytes || !aligned16(workspace))
+    return DUSTIN_OK;
+}
+
+// Workspace of a set of signals: each signal's layout, one after the other.
+size_t signals_workspace(int B, int n_max, int n_sig, const dustin_srh_signal *sigs, size_t *offs)
+{
+    size_t off = 0;
+    for (int s = 0; s < n_sig; ++s) {
+        int tq = 0;
+        for (int i = 0; i < sigs[s].n_groups; ++i)
+            tq += sigs[s].groups[i].n_qheads;
+        if (offs)
+            offs[s] = off;
+        off += align_up(score_workspace(B, n_max, tq, sigs[s].n_q, sigs[s].mode).bytes);
+    }
+    return off;
+}
+
+dustin_status run_score(int B, int n_max, const int32_t *ctx_len, int n_sig, const dustin_srh_signal *sigs,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (B < 0 || n_max < 0 || n_sig < 1 || n_sig > kMaxSignals || !sigs)
+        return DUSTIN_ERR_INVALID_ARG;
+    int tq[kMaxSignals], mp[kMaxSignals], cc[kMaxSignals], groups = 0;
+    for (int s = 0; s < n_sig; ++s) {
+        const dustin_status st = check_signal(sigs[s], tq[s], mp[s], cc[s], n_max);
+        if (st != DUSTIN_OK)
+            return st;
+        groups += sigs[s].n_groups;
+    }
+    if (groups > kMaxGroups)
+        return DUSTIN_ERR_UNSUPPORTED;
+    if (B == 0 || n_max == 0)
+        return DUSTIN_OK;
+    if (!ctx_len)
+        return DUSTIN_ERR_INVALID_ARG;
+    for (int s = 0; s < n_sig; ++s)
+        if (!sigs[s].q || !sigs[s].score || !aligned16(sigs[s].q) || !aligned16(sigs[s].score))
+            return DUSTIN_ERR_INVALID_ARG;
+    size_t offs[kMaxSignals];
+    const size_t need = signals_workspace(B, n_max, n_sig, sigs, offs);
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
         return DUSTIN_ERR_WORKSPACE;
 
     ScoreArgs a;
     a.B = B;
     a.n_max = n_max;
-    a.n_pad = lay.n_pad;
-    a.n_groups = n_groups;
-    a.n_q = n_q;
-    a.mode = mode;
-    a.total_qheads = total_qheads;
-    a.total_pairs = lay.total_pairs;
-    a.logit_rows = mode == DUSTIN_SCORE_PROB_SUM ? lay.total_pairs : n_groups;
-    a.n_tiles = lay.n_tiles;
-    a.n_parts = lay.n_parts;   // the most the workspace holds; the launch picks its count
-    a.ctx_clamp = ctx_clamp;
+    a.n_sig = n_sig;
+    a.prob_g0 = 0;
     a.ctx_len = ctx_len;
-    a.q = static_cast<const uint16_t *>(q);
-    a.mul = mode == DUSTIN_SCORE_PROB_SUM ? (double)scale * 1.4426950408889634 : (double)scale;
-    a.logits = reinterpret_cast<float *>(static_cast<char *>(workspace) + lay.logits_off);
-    a.tile_max = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.max_off);
-    a.tile_sum = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.tsum_off);
-    a.part_max = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.pmax_off);
-    a.part_sum = reinterpret_cast<double *>(static_cast<char *>(workspace) + lay.psum_off);
-    a.score = score;
-    int qh = 0, pr = 0;
-    for (int i = 0; i < n_groups; ++i) {
-        ScoreGroup &sg = a.grp[i];
-        sg.k = make_view(groups[i].k);
-        sg.kv_head = groups[i].kv_head;
-        sg.q_head0 = qh;
-        sg.n_qheads = groups[i].n_qheads;
-        sg.pair0 = pr;
-        sg.n_pairs = groups[i].n_qheads * ppq;
-        qh += sg.n_qheads;
-        pr += sg.n_pairs;
+    int g0 = 0;
+    for (int s = 0; s < n_sig; ++s) {
+        const dustin_srh_signal &in = sigs[s];
+        const ScoreWs lay = score_workspace(B, n_max, tq[s], in.n_q, in.mode);
+        char *base = static_cast<char *>(workspace) + offs[s];
+        a.n_pad = lay.n_pad;       // the same for every signal (n_max)
+        a.n_tiles = lay.n_tiles;
+        a.n_parts = lay.n_parts;   // the most the workspace holds; the launch picks its count
+        ScoreSig &S = a.sig[s];
+        S.n_groups = in.n_groups;
+        S.g0 = g0;
+        S.n_q = in.n_q;
+        S.mode = in.mode;
+        S.total_qheads = tq[s];
+        S.total_pairs = lay.total_pairs;
+        S.head_dim = in.head_dim;
+        S.ctx_clamp = cc[s];
+        S.logit_rows = in.mode == DUSTIN_SCORE_PROB_SUM ? lay.total_pairs : in.n_groups;
+        S.q = static_cast<const uint16_t *>(in.q);
+        S.mul = in.mode == DUSTIN_SCORE_PROB_SUM ? (double)in.scale * 1.4426950408889634 : (double)in.scale;
+        S.logits = reinterpret_cast<float *>(base + lay.logits_off);
+        S.tile_max = reinterpret_cast<double *>(base + lay.max_off);
+        S.tile_sum = reinterpret_cast<double *>(base + lay.tsum_off);
+        S.part_max = reinterpret_cast<double *>(base + lay.pmax_off);
+        S.part_sum = reinterpret_cast<double *>(base + lay.psum_off);
+        S.score = in.score;
+        const int ppq = pairs_per_qhead(in.n_q, in.mode);
+        int qh = 0, pr = 0;
+        for (int i = 0; i < in.n_groups; ++i) {
+            ScoreGroup &sg = a.grp[g0 + i];
+            sg.k = make_view(in.groups[i].k);
+            sg.kv_head = in.groups[i].kv_head;
+            sg.sig = s;
+            sg.q_head0 = qh;
+            sg.n_qheads = in.groups[i].n_qheads;
+            sg.pair0 = pr;
+            sg.n_pairs = in.groups[i].n_qheads * ppq;
+            qh += sg.n_qheads;
+            pr += sg.n_pairs;
+        }
+        g0 += in.n_groups;
     }
-    const hipError_t e = launch_score(a, head_dim, max_pairs, device_cus(), static_cast<hipStream_t>(stream));
+    const hipError_t e = launch_score(a, device_cus(), static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
+}
+
+}  // namespace
+
+dustin_status dustin_srh_score(int B, int n_max, const int32_t *ctx_len, int n_groups,
+                               const dustin_srh_group *groups, int head_dim, const void *q, int n_q,
+                               float scale, int mode, float *score, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    dustin_srh_signal sg;
+    sg.n_groups = n_groups;
+    sg.groups = groups;
+    sg.head_dim = head_dim;
+    sg.q = q;
+    sg.n_q = n_q;
+    sg.scale = scale;
+    sg.mode = mode;
+    sg.score = score;
+    return run_score(B, n_max, ctx_len, 1, &sg, workspace, workspace_bytes, stream);
+}
+
+dustin_status dustin_srh_score_signals_workspace_size(int B, int n_max, int n_signals,
+                                                      const dustin_srh_signal *signals, size_t *bytes)
+{
+    if (!bytes || B < 0 || n_max < 0 || n_signals < 1 || n_signals > kMaxSignals || !signals)
+        return DUSTIN_ERR_INVALID_ARG;
+    int groups = 0;
+    for (int s = 0; s < n_signals; ++s) {
+        int tq, mp, cc;
+        const dustin_status st = check_signal(signals[s], tq, mp, cc, n_max);
+        if (st != DUSTIN_OK)
+            return st;
+        groups += signals[s].n_groups;
+    }
+    if (groups > kMaxGroups)
+        return DUSTIN_ERR_UNSUPPORTED;
+    *bytes = signals_workspace(B, n_max, n_signals, signals, nullptr);
+    return DUSTIN_OK;
+}
+
+dustin_status dustin_srh_score_signals(int B, int n_max, const int32_t *ctx_len, int n_signals,
+                                       const dustin_srh_signal *signals, void *workspace,
+                                       size_t workspace_bytes, void *stream)
+{
+    return run_score(B, n_max, ctx_len, n_signals, signals, workspace, workspace_bytes, stream);
 }
 
 dustin_status dustin_select_workspace_size(int B, int n_max, size_t *bytes)

@@ -63,18 +63,22 @@ constexpr int kScoreParts = 64;   // most workgroups per (group, sequence) of th
 struct ScoreGroup {
     KvView k;
     int kv_head;
-    int q_head0;      // first query head of the group in q
+    int sig;          // the signal the group belongs to
+    int q_head0;      // first query head of the group in the signal's q
     int n_qheads;
-    int pair0;        // first pair of the group in the logit workspace
+    int pair0;        // first pair of the group in the signal's logit workspace
     int n_pairs;
+    int parts;        // softmax mode: workgroups per sequence sharing the group's tiles
+    int wg0;          // softmax mode: first workgroup of the group (then b * parts + part)
 };
 
-struct ScoreArgs {
-    int B, n_max, n_pad, n_groups, n_q, mode, total_qheads, total_pairs, n_tiles, n_parts, ctx_clamp;
+// One scored signal (draft lookahead or target historical queries).
+struct ScoreSig {
+    int n_groups, g0;        // its groups: grp[g0 .. g0 + n_groups)
+    int n_q, mode, total_qheads, total_pairs, head_dim, ctx_clamp;
     int logit_rows;          // rows per sequence of `logits`: total_pairs (PROB_SUM), n_groups
-    const int32_t *ctx_len;
     const uint16_t *q;
-    double mul;              // PROB_SUM: scale*log2(e) (base-2 logits); LOGIT_SUM2: scale
+    double mul;              // PROB_SUM: scale*log2(e) (base-2 logits); logit sums: scale
     float *logits;           // [B][logit_rows][n_pad]: PROB_SUM l - tile max per pair; logit-sum
                              //   modes: per group, the sum of its pairs' logits
     double *tile_max;        // PROB_SUM: [B][total_pairs][n_tiles], n_tiles = ceil(n_max / kStatTile)
@@ -82,11 +86,20 @@ struct ScoreArgs {
     double *part_max;        // PROB_SUM: [B][total_pairs][n_parts], one (max, sum of exp2(l - max))
     double *part_sum;        //   per workgroup of the logit kernel
     float *score;            // [B][n_max]
+};
+
+constexpr int kMaxSignals = 2;
+
+struct ScoreArgs {
+    int B, n_max, n_pad, n_tiles, n_parts, n_sig;
+    int prob_g0, prob_ng;    // the softmax-mode launch covers grp[prob_g0 .. prob_g0 + prob_ng)
+    const int32_t *ctx_len;
+    ScoreSig sig[kMaxSignals];
     ScoreGroup grp[kMaxGroups];
 };
 
 // cus: compute units of the device (sizes the softmax-mode grid to one resident round)
-hipError_t launch_score(ScoreArgs a, int head_dim, int max_pairs, int cus, hipStream_t st);
+hipError_t launch_score(ScoreArgs a, int cus, hipStream_t st);
 
 // ---------------------------------------------------------------- selection
 constexpr int kSelectThreads = 1024;

@@ -122,26 +122,28 @@ __device__ __forceinline__ void column_reduce_f32(float (&v)[N])
     }
 }
 
+// LDS bytes of one wave's staged tile at head dim D (row stride 2D + 16: conflict-free
+// 16-byte row reads)
+__host__ __device__ constexpr int prob_tile_bytes(int D) { return kStatTile * (2 * D + 16); }
+
+// One workgroup of the softmax-mode logit kernel for group G (head dim D).  sK: the waves'
+// tile areas (kProbWaves x prob_tile_bytes(D)); sNext: the workgroup's tile counter.
 // FLAT: every group's view is unpaged with a row stride below 4 GiB, so a row address is a
 // per-workgroup base plus token x stride (one 32x32->64 multiply-add per load).
 template <int D, bool FLAT>
-__global__ __launch_bounds__(64 * kProbWaves)
-__attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel(ScoreArgs a)
+__device__ __forceinline__ void prob_logits(const ScoreArgs &a, const ScoreGroup &G, int b, int part, uint8_t *sK,
+                                            int &sNext)
 {
     constexpr int NW = kProbWaves;
     constexpr int NT = 64 * NW;
     constexpr int KS = D / 32;          // MFMA k-steps of a row (32 elements each)
     constexpr int kDepth = FLAT ? 2 : 1;   // tiles in flight in registers per wave
     constexpr int RB = D * 2;           // bytes per key row
-    constexpr int RSTR = RB + 16;       // LDS row stride (conflict-free 16-byte row reads)
+    constexpr int RSTR = RB + 16;       // LDS row stride
     constexpr int CPR = RB / 16;        // 16-byte chunks per row
     constexpr int LPT = kStatTile * CPR / 64;   // 16-byte loads per lane per 64-token tile
-    __shared__ __align__(16) uint8_t sK[NW][kStatTile * RSTR];   // one tile per wave
-    __shared__ int sNext;               // tiles claimed so far by the workgroup's waves
-
-    const ScoreGroup &G = a.grp[blockIdx.y];
-    const int b = blockIdx.z;
-    const int N = clampi(a.ctx_len[b], 0, a.ctx_clamp);
+    const ScoreSig &S = a.sig[G.sig];
+    const int N = clampi(a.ctx_len[b], 0, S.ctx_clamp);
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -149,20 +151,20 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
     const int li = lane & 15;
     // 64-token tiles holding context tokens; this workgroup takes an equal share of them
     const int n_live = (N + kStatTile - 1) / kStatTile;
-    const int q_lo = (int)((int64_t)n_live * blockIdx.x / gridDim.x);
-    const int q_hi = (int)((int64_t)n_live * (blockIdx.x + 1) / gridDim.x);
+    const int q_lo = (int)((int64_t)n_live * part / G.parts);
+    const int q_hi = (int)((int64_t)n_live * (part + 1) / G.parts);
 
     // statistics tiles past the live tiles: empty
-    for (int st = n_live + blockIdx.x; st < a.n_tiles; st += gridDim.x)
+    for (int st = n_live + part; st < a.n_tiles; st += G.parts)
         for (int p = tid; p < G.n_pairs; p += NT) {
-            const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_tiles + st;
-            a.tile_max[e] = -INFINITY;
+            const int64_t e = ((int64_t)b * S.total_pairs + G.pair0 + p) * a.n_tiles + st;
+            S.tile_max[e] = -INFINITY;
         }
     if (q_lo >= q_hi) {
         for (int p = tid; p < G.n_pairs; p += NT) {
-            const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_parts + blockIdx.x;
-            a.part_max[e] = -INFINITY;
-            a.part_sum[e] = 0.0;
+            const int64_t e = ((int64_t)b * S.total_pairs + G.pair0 + p) * a.n_parts + part;
+            S.part_max[e] = -INFINITY;
+            S.part_sum[e] = 0.0;
         }
         return;
     }
@@ -173,9 +175,9 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
         const int p = li;
         const uint16_t *qp = nullptr;
         if (p < G.n_pairs) {
-            const int hl = p / a.n_q;
-            const int j = p - hl * a.n_q;
-            qp = a.q + ((int64_t)(b * a.total_qheads + G.q_head0 + hl) * a.n_q + j) * D + quad * 8;
+            const int hl = p / S.n_q;
+            const int j = p - hl * S.n_q;
+            qp = S.q + ((int64_t)(b * S.total_qheads + G.q_head0 + hl) * S.n_q + j) * D + quad * 8;
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -184,7 +186,7 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
     if (tid == 0)
         sNext = 0;
     __syncthreads();                  // the tile counter ready
-    uint8_t *myK = sK[w];
+    uint8_t *myK = sK + w * prob_tile_bytes(D);
 
     // A wave's tile is 64 tokens: lane l loads chunks l + 64 i (row = chunk / CPR) of the
     // tile's rows (whole rows per instruction: the coalescing the matrix-core operand
@@ -265,7 +267,7 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
         for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                lp[rb][r] = tok0 + 16 * rb + r < N ? lg[rb][r] * a.mul : -INFINITY;
+                lp[rb][r] = tok0 + 16 * rb + r < N ? lg[rb][r] * S.mul : -INFINITY;
                 red[0] = fmaxf(red[0], (float)lp[rb][r]);
             }
         column_reduce_f32<1, true>(red);
@@ -282,17 +284,17 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
             }
         column_reduce_f32<1, false>(red);
         if (li < G.n_pairs) {
-            const int64_t row = (int64_t)b * a.total_pairs + G.pair0 + li;
+            const int64_t row = (int64_t)b * S.total_pairs + G.pair0 + li;
             // four consecutive tokens per store; tok0 + 16 rb < N <= n_pad, both multiples
             // of four, so the four stay inside the row
 #pragma unroll
             for (int rb = 0; rb < 4; ++rb)
                 if (tok0 + 16 * rb < N)
-                    *reinterpret_cast<f32x4 *>(a.logits + row * a.n_pad + tok0 + 16 * rb) =
+                    *reinterpret_cast<f32x4 *>(S.logits + row * a.n_pad + tok0 + 16 * rb) =
                         f32x4{off[rb][0], off[rb][1], off[rb][2], off[rb][3]};
             if (quad == 0 && tile < a.n_tiles) {
-                a.tile_max[row * a.n_tiles + tile] = (double)mx;
-                a.tile_sum[row * a.n_tiles + tile] = (double)red[0];
+                S.tile_max[row * a.n_tiles + tile] = (double)mx;
+                S.tile_sum[row * a.n_tiles + tile] = (double)red[0];
             }
         }
     };
@@ -332,10 +334,10 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
     // values of a tile requested together), then the lanes combined by a fixed butterfly.
     __syncthreads();                  // every tile's (max, sum) is stored
     for (int p = w; p < G.n_pairs; p += NW) {
-        const int64_t row = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_tiles;
+        const int64_t row = ((int64_t)b * S.total_pairs + G.pair0 + p) * a.n_tiles;
         double Ml = -INFINITY, Sl = 0.0;
         for (int t = q_lo + lane; t < q_hi; t += 64) {
-            const double m = a.tile_max[row + t], sm = a.tile_sum[row + t];
+            const double m = S.tile_max[row + t], sm = S.tile_sum[row + t];
             if (m > -INFINITY) {
                 const double M1 = fmax(Ml, m);
                 Sl = (Ml > -INFINITY ? Sl * (double)fast_exp2((float)(Ml - M1)) : 0.0) +
@@ -344,15 +346,45 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
             }
         }
         const double M = wave_max_f64_dpp(Ml);
-        double S = Ml > -INFINITY ? Sl * (double)fast_exp2((float)(Ml - M)) : 0.0;
+        double Z = Ml > -INFINITY ? Sl * (double)fast_exp2((float)(Ml - M)) : 0.0;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1)
-            S += __shfl_xor(S, o);
+            Z += __shfl_xor(Z, o);
         if (lane == 0) {
-            const int64_t e = ((int64_t)b * a.total_pairs + G.pair0 + p) * a.n_parts + blockIdx.x;
-            a.part_max[e] = M;
-            a.part_sum[e] = S;
+            const int64_t e = ((int64_t)b * S.total_pairs + G.pair0 + p) * a.n_parts + part;
+            S.part_max[e] = M;
+            S.part_sum[e] = Z;
         }
+    }
+}
+
+
+// DM: the head dim of every group launched (64 or 128), or 0 when the launch holds groups
+// of both head dims (each workgroup then takes its group's path; the LDS is sized for 128).
+template <int DM, bool FLAT>
+__global__ __launch_bounds__(64 * kProbWaves)
+__attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel(ScoreArgs a)
+{
+    __shared__ __align__(16) uint8_t sK[kProbWaves * prob_tile_bytes(DM == 64 ? 64 : 128)];
+    __shared__ int sNext;               // tiles claimed so far by the workgroup's waves
+    // workgroup -> (group, sequence, part): the groups' workgroups are consecutive ranges
+    const int x = blockIdx.x;
+    int gi = a.prob_g0;
+    for (int g = a.prob_g0 + 1; g < a.prob_g0 + a.prob_ng; ++g)
+        gi = x >= a.grp[g].wg0 ? g : gi;
+    const ScoreGroup &G = a.grp[gi];
+    const int r = x - G.wg0;
+    const int b = r / G.parts;
+    const int part = r - b * G.parts;
+    if constexpr (DM == 64) {
+        prob_logits<64, FLAT>(a, G, b, part, sK, sNext);
+    } else if constexpr (DM == 128) {
+        prob_logits<128, FLAT>(a, G, b, part, sK, sNext);
+    } else {
+        if (a.sig[G.sig].head_dim == 64)
+            prob_logits<64, FLAT>(a, G, b, part, sK, sNext);
+        else
+            prob_logits<128, FLAT>(a, G, b, part, sK, sNext);
     }
 }
 
@@ -363,13 +395,14 @@ constexpr int kSub = kPerWave / 16;
 constexpr int kBatch = 4;
 
 template <int D, int PT>
-__global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
+__global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a, int sidx)
 {
     constexpr int KS = D / 32;
     const int tile = blockIdx.x;
-    const ScoreGroup &G = a.grp[blockIdx.y];
+    const ScoreSig &S = a.sig[sidx];
+    const ScoreGroup &G = a.grp[S.g0 + blockIdx.y];
     const int b = blockIdx.z;
-    const int N = clampi(a.ctx_len[b], 0, a.ctx_clamp);
+    const int N = clampi(a.ctx_len[b], 0, S.ctx_clamp);
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -380,9 +413,9 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
         return;
     // pair p of the group = (query head p / nqe, query p % nqe); LOGIT_SUM2 maps the
     // second query slot to the last query
-    const bool all_q = a.mode == DUSTIN_SCORE_LOGIT_SUM_ALL;
-    const int nqe = all_q ? a.n_q : min(2, a.n_q);
-    const float mul = (float)a.mul;
+    const bool all_q = S.mode == DUSTIN_SCORE_LOGIT_SUM_ALL;
+    const int nqe = all_q ? S.n_q : min(2, S.n_q);
+    const float mul = (float)S.mul;
 
     // SRH queries as the MFMA B operand: lane holds pair pt*16 + li, its quarter of d
     u32x4 qop[PT][KS];
@@ -392,9 +425,9 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
         if (p < G.n_pairs) {
             const int hl = p / nqe;
             const int jj = p - hl * nqe;
-            const int j = all_q || jj == 0 ? jj : a.n_q - 1;
+            const int j = all_q || jj == 0 ? jj : S.n_q - 1;
             const uint16_t *qp =
-                a.q + ((int64_t)(b * a.total_qheads + G.q_head0 + hl) * a.n_q + j) * D + quad * (D / 4);
+                S.q + ((int64_t)(b * S.total_qheads + G.q_head0 + hl) * S.n_q + j) * D + quad * (D / 4);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 qop[pt][ks] = load16(qp + ks * 8);
@@ -439,7 +472,7 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a)
             }
             row16_reduce_f32<4, false>(c);
             if (li == 0 && tb < N) {
-                float *dst = a.logits + ((int64_t)b * a.logit_rows + blockIdx.y) * a.n_pad + tb;
+                float *dst = S.logits + ((int64_t)b * S.logit_rows + blockIdx.y) * a.n_pad + tb;
                 if (tb + 3 < N) {
                     *reinterpret_cast<f32x4 *>(dst) = f32x4{c[0], c[1], c[2], c[3]};
                 } else {
@@ -463,17 +496,18 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
     static_assert(kFinTokens == 4 * kThreads, "one f32x4 of tokens per thread");
     __shared__ float sOff[kMaxGroups * kMaxProbPairsPerGroup][kFinTiles];
     __shared__ float sInvZ[kMaxGroups * kMaxProbPairsPerGroup];
+    const ScoreSig &S = a.sig[blockIdx.z];
     const int b = blockIdx.y;
     const int tid = threadIdx.x;
-    const int N = clampi(a.ctx_len[b], 0, a.ctx_clamp);
-    const bool prob = a.mode == DUSTIN_SCORE_PROB_SUM;
+    const int N = clampi(a.ctx_len[b], 0, S.ctx_clamp);
+    const bool prob = S.mode == DUSTIN_SCORE_PROB_SUM;
     const int tile0 = blockIdx.x * kFinTiles;
     // this thread's 4 tokens: the logits of the first kFinChunk pairs are requested before
     // the statistics (which do not need them), all in one round of loads
-    const int P = prob ? a.total_pairs : a.n_groups;   // logit rows summed per token
+    const int P = prob ? S.total_pairs : S.n_groups;   // logit rows summed per token
     const int tb = blockIdx.x * kFinTokens + tid * 4;
     const bool live = tb < N;
-    const float *lg = a.logits + (int64_t)b * a.logit_rows * a.n_pad + tb;
+    const float *lg = S.logits + (int64_t)b * S.logit_rows * a.n_pad + tb;
     f32x4 lv[kFinChunk];
     auto fetch = [&](int p0) {
 #pragma unroll
@@ -490,16 +524,20 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
         // kFinTiles the maxima of this block's statistics tiles
         const int w = tid >> 6, lane = tid & 63;
         const int t = tile0 + lane;
-        for (int p0 = w; p0 < a.total_pairs; p0 += 4 * kFinBatch) {
+        for (int p0 = w; p0 < S.total_pairs; p0 += 4 * kFinBatch) {
             double pm[kFinBatch], ps[kFinBatch], tm[kFinBatch];
 #pragma unroll
             for (int k = 0; k < kFinBatch; ++k) {
                 const int p = p0 + 4 * k;
-                const int64_t row = (int64_t)b * a.total_pairs + p;
-                const bool ok = p < a.total_pairs;
-                pm[k] = ok && lane < a.n_parts ? a.part_max[row * a.n_parts + lane] : -INFINITY;
-                ps[k] = ok && lane < a.n_parts ? a.part_sum[row * a.n_parts + lane] : 0.0;
-                tm[k] = ok && lane < kFinTiles && t < a.n_tiles ? a.tile_max[row * a.n_tiles + t] : -INFINITY;
+                const int64_t row = (int64_t)b * S.total_pairs + p;
+                const bool ok = p < S.total_pairs;
+                // the workgroups that shared the tiles of the pair's group
+                int np = 1;
+                for (int g = S.g0; g < S.g0 + S.n_groups; ++g)
+                    np = p >= a.grp[g].pair0 ? a.grp[g].parts : np;
+                pm[k] = ok && lane < np ? S.part_max[row * a.n_parts + lane] : -INFINITY;
+                ps[k] = ok && lane < np ? S.part_sum[row * a.n_parts + lane] : 0.0;
+                tm[k] = ok && lane < kFinTiles && t < a.n_tiles ? S.tile_max[row * a.n_tiles + t] : -INFINITY;
             }
 #pragma unroll
             for (int k = 0; k < kFinBatch; ++k) {
@@ -509,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
 #pragma unroll
                 for (int o = 32; o > 0; o >>= 1)
                     Z += __shfl_xor(Z, o);
-                if (p < a.total_pairs) {
+                if (p < S.total_pairs) {
                     if (lane == 0)
                         sInvZ[p] = Z > 0.0 ? (float)(1.0 / Z) : 0.f;
                     if (lane < kFinTiles)
@@ -545,7 +583,7 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
     for (int r = 0; r < 4; ++r)
         if (tb + r >= N)
             v[r] = 0.f;
-    float *dst = a.score + (int64_t)b * a.n_max + tb;
+    float *dst = S.score + (int64_t)b * a.n_max + tb;
     if ((a.n_max & 3) == 0) {
         *reinterpret_cast<f32x4 *>(dst) = v;
     } else {
@@ -557,73 +595,103 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
 }
 
 template <int D>
-hipError_t launch_logit_sum(const ScoreArgs &a, int pt, dim3 grid, hipStream_t st)
+hipError_t launch_logit_sum(const ScoreArgs &a, int sidx, int pt, dim3 grid, hipStream_t st)
 {
     switch (pt) {
-    case 1: hipLaunchKernelGGL((srh_logit_sum_kernel<D, 1>), grid, dim3(kThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((srh_logit_sum_kernel<D, 2>), grid, dim3(kThreads), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((srh_logit_sum_kernel<D, 3>), grid, dim3(kThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((srh_logit_sum_kernel<D, 4>), grid, dim3(kThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((srh_logit_sum_kernel<D, 1>), grid, dim3(kThreads), 0, st, a, sidx); break;
+    case 2: hipLaunchKernelGGL((srh_logit_sum_kernel<D, 2>), grid, dim3(kThreads), 0, st, a, sidx); break;
+    case 3: hipLaunchKernelGGL((srh_logit_sum_kernel<D, 3>), grid, dim3(kThreads), 0, st, a, sidx); break;
+    default: hipLaunchKernelGGL((srh_logit_sum_kernel<D, 4>), grid, dim3(kThreads), 0, st, a, sidx); break;
     }
     return hipGetLastError();
 }
 
-// The softmax-mode kernel.  Its grid is one resident round: as many workgroups per CU as
-// the variant's registers and LDS allow (asked of the runtime once per variant), each
-// taking an equal share of its stream's tiles.  a.n_parts comes in as the workspace's
-// maximum and leaves as the count launched (the finalize reads that many).
-template <int D, bool FLAT>
+// The softmax-mode kernel over the softmax-mode signals' groups (grp[a.prob_g0 ..
+// + n_groups)).  Its grid is one resident round: as many workgroups per CU as the
+// variant's registers and LDS allow (asked of the runtime once per variant), each taking
+// an equal share of its stream's tiles.  a.n_parts comes in as the workspace's maximum and
+// leaves as the count launched (the finalize reads that many).
+template <int DM, bool FLAT>
 hipError_t launch_prob_variant(ScoreArgs &a, int cus, hipStream_t st)
 {
     constexpr int nt = 64 * kProbWaves;
     static const int per_cu = [] {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, srh_prob_logits_kernel<D, FLAT>, nt, 0) != hipSuccess ||
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, srh_prob_logits_kernel<DM, FLAT>, nt, 0) !=
+                hipSuccess ||
             n < 1)
             n = 1;
         return n;
     }();
-    const int ws = a.n_groups * a.B;
-    a.n_parts = std::max(1, std::min(a.n_parts, (per_cu * cus + ws - 1) / ws));
-    const dim3 grid((unsigned)a.n_parts, (unsigned)a.n_groups, (unsigned)a.B);
-    hipLaunchKernelGGL((srh_prob_logits_kernel<D, FLAT>), grid, dim3(nt), 0, st, a);
+    // one resident round of workgroups, shared among the groups in proportion to their
+    // bytes per token (the head dim), at least one and at most the workspace's count each
+    const int slots = std::max(1, per_cu * cus / std::max(1, a.B));
+    int dsum = 0;
+    for (int g = a.prob_g0; g < a.prob_g0 + a.prob_ng; ++g)
+        dsum += a.sig[a.grp[g].sig].head_dim;
+    int wg = 0, pmax = 1;
+    for (int g = a.prob_g0; g < a.prob_g0 + a.prob_ng; ++g) {
+        ScoreGroup &G = a.grp[g];
+        const int d = a.sig[G.sig].head_dim;
+        G.parts = std::max(1, std::min(a.n_parts, (slots * d + dsum / 2) / dsum));
+        G.wg0 = wg;
+        wg += G.parts * a.B;
+        pmax = std::max(pmax, G.parts);
+    }
+    a.n_parts = pmax;
+    hipLaunchKernelGGL((srh_prob_logits_kernel<DM, FLAT>), dim3((unsigned)wg), dim3(nt), 0, st, a);
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_prob(ScoreArgs &a, int max_pairs, int cus, hipStream_t st)
+template <int DM>
+hipError_t launch_prob(ScoreArgs &a, bool flat, int cus, hipStream_t st)
 {
-    if (max_pairs > 16)
-        return hipErrorInvalidValue;
-    bool flat = true;
-    for (int g = 0; g < a.n_groups; ++g)
-        flat = flat && !a.grp[g].k.pt && a.grp[g].k.st >= 0 && a.grp[g].k.st * 2 < (int64_t)1 << 32;
-    return flat ? launch_prob_variant<D, true>(a, cus, st) : launch_prob_variant<D, false>(a, cus, st);
+    return flat ? launch_prob_variant<DM, true>(a, cus, st) : launch_prob_variant<DM, false>(a, cus, st);
 }
 
 }  // namespace
 
-hipError_t launch_score(ScoreArgs a, int head_dim, int max_pairs, int cus, hipStream_t st)
+// Softmax-mode signals share one logit launch (their groups are contiguous: signals are
+// stored in order); each logit-sum signal has its own; one finalize launch serves every
+// signal (grid z = signal).
+hipError_t launch_score(ScoreArgs a, int cus, hipStream_t st)
 {
     hipError_t e = hipSuccess;
-    if (a.mode == DUSTIN_SCORE_PROB_SUM) {
-        if (head_dim == 64)
-            e = launch_prob<64>(a, max_pairs, cus, st);
-        else
-            e = launch_prob<128>(a, max_pairs, cus, st);
-        if (e != hipSuccess)
-            return e;
-    } else {
-        const dim3 g1((unsigned)((a.n_max + kSumTile - 1) / kSumTile), (unsigned)a.n_groups, (unsigned)a.B);
-        const int pt = (max_pairs + 15) / 16;
-        e = head_dim == 64 ? launch_logit_sum<64>(a, pt, g1, st) : launch_logit_sum<128>(a, pt, g1, st);
+    int pg0 = -1, png = 0, dims = 0;
+    bool flat = true;
+    for (int s = 0; s < a.n_sig; ++s) {
+        const ScoreSig &S = a.sig[s];
+        if (S.mode != DUSTIN_SCORE_PROB_SUM)
+            continue;
+        if (pg0 < 0)
+            pg0 = S.g0;
+        png += S.n_groups;
+        dims |= S.head_dim == 64 ? 1 : 2;
+        for (int g = S.g0; g < S.g0 + S.n_groups; ++g)
+            flat = flat && !a.grp[g].k.pt && a.grp[g].k.st >= 0 && a.grp[g].k.st * 2 < (int64_t)1 << 32;
+    }
+    if (png > 0) {
+        a.prob_g0 = pg0;
+        a.prob_ng = png;
+        e = dims == 1 ? launch_prob<64>(a, flat, cus, st)
+                      : (dims == 2 ? launch_prob<128>(a, flat, cus, st) : launch_prob<0>(a, flat, cus, st));
         if (e != hipSuccess)
             return e;
     }
-    e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    const dim3 g2((unsigned)((a.n_max + kFinTokens - 1) / kFinTokens), (unsigned)a.B);
+    for (int s = 0; s < a.n_sig; ++s) {
+        const ScoreSig &S = a.sig[s];
+        if (S.mode == DUSTIN_SCORE_PROB_SUM)
+            continue;
+        int max_pairs = 1;
+        for (int g = S.g0; g < S.g0 + S.n_groups; ++g)
+            max_pairs = std::max(max_pairs, a.grp[g].n_pairs);
+        const dim3 g1((unsigned)((a.n_max + kSumTile - 1) / kSumTile), (unsigned)S.n_groups, (unsigned)a.B);
+        const int pt = (max_pairs + 15) / 16;
+        e = S.head_dim == 64 ? launch_logit_sum<64>(a, s, pt, g1, st) : launch_logit_sum<128>(a, s, pt, g1, st);
+        if (e != hipSuccess)
+            return e;
+    }
+    const dim3 g2((unsigned)((a.n_max + kFinTokens - 1) / kFinTokens), (unsigned)a.B, (unsigned)a.n_sig);
     hipLaunchKernelGGL(srh_finalize_kernel, g2, dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }

@@ -51,6 +51,12 @@ class SrhGroup(ctypes.Structure):
     _fields_ = [("k", KvView), ("kv_head", ctypes.c_int32), ("n_qheads", ctypes.c_int32)]
 
 
+class SrhSignal(ctypes.Structure):
+    _fields_ = [("n_groups", ctypes.c_int32), ("groups", ctypes.POINTER(SrhGroup)), ("head_dim", ctypes.c_int32),
+                ("q", _P), ("n_q", ctypes.c_int32), ("scale", ctypes.c_float), ("mode", ctypes.c_int32),
+                ("score", _P)]
+
+
 def _decl(name, args):
     f = getattr(_lib, name)
     f.argtypes = args
@@ -63,6 +69,9 @@ _lib.dustin_status_string.restype = ctypes.c_char_p
 _score_ws = _decl("dustin_srh_score_workspace_size", [_I, _I, _I, _I, _I, ctypes.POINTER(_SZ)])
 _score = _decl("dustin_srh_score", [_I, _I, _P, _I, ctypes.POINTER(SrhGroup), _I, _P, _I, _F, _I,
                                     _P, _P, _SZ, _P])
+_signals_ws = _decl("dustin_srh_score_signals_workspace_size", [_I, _I, _I, ctypes.POINTER(SrhSignal),
+                                                               ctypes.POINTER(_SZ)])
+_signals = _decl("dustin_srh_score_signals", [_I, _I, _P, _I, ctypes.POINTER(SrhSignal), _P, _SZ, _P])
 _select_ws = _decl("dustin_select_workspace_size", [_I, _I, ctypes.POINTER(_SZ)])
 _select = _decl("dustin_select", [_I, _I, _P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _SZ, _P])
 _sparse_ws = _decl("dustin_sparse_verify_attn_workspace_size", [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_SZ)])
@@ -85,6 +94,7 @@ _kv_commit = _decl("dustin_kv_commit", [_I, _I, _P, _P, _P])
 _recovery = _decl("dustin_attn_recovery", [_I, _P, _P, _P, _P])
 
 EXPORTED = ("dustin_status_string", "dustin_srh_score_workspace_size", "dustin_srh_score",
+            "dustin_srh_score_signals_workspace_size", "dustin_srh_score_signals",
             "dustin_select_workspace_size", "dustin_select",
             "dustin_sparse_verify_attn_workspace_size", "dustin_sparse_verify_attn",
             "dustin_sparse_verify_attn_noalloc", "dustin_attn_plan", "dustin_sparse_verify_attn_logits",
@@ -177,6 +187,50 @@ def dustin_srh_score(ctx_len: torch.Tensor, groups: Sequence[Tuple[KvView, int, 
         raise ValueError("q must be contiguous bf16, score contiguous fp32")
     _check(_score(B, n_max, _ptr(ctx_len), len(groups), arr, d, _ptr(q), n_q, float(scale), mode,
                   _ptr(score), _ptr(ws), ws.numel(), _stream(stream)), "dustin_srh_score")
+
+
+def _signal_array(signals, B):
+    """signals: (groups, q, scale, mode, score) per signal -> (SrhSignal array, keep-alive)."""
+    arr = (SrhSignal * len(signals))()
+    keep = []
+    for i, (groups, q, scale, mode, score) in enumerate(signals):
+        g = (SrhGroup * len(groups))()
+        for j, (view, kv_head, nqh) in enumerate(groups):
+            g[j].k = view
+            g[j].kv_head = kv_head
+            g[j].n_qheads = nqh
+        keep.append(g)
+        if q.dtype != torch.bfloat16 or not q.is_contiguous() or score.dtype != torch.float32 \
+                or not score.is_contiguous() or q.shape[0] != B:
+            raise ValueError("q must be contiguous bf16 [B][heads][n_q][d], score contiguous fp32 [B][n_max]")
+        arr[i].n_groups = len(groups)
+        arr[i].groups = ctypes.cast(g, ctypes.POINTER(SrhGroup))
+        arr[i].head_dim = q.shape[3]
+        arr[i].q = q.data_ptr()
+        arr[i].n_q = q.shape[2]
+        arr[i].scale = float(scale)
+        arr[i].mode = int(mode)
+        arr[i].score = score.data_ptr()
+    return arr, keep
+
+
+def dustin_srh_score_signals_workspace_size(B: int, n_max: int, signals) -> int:
+    """signals: (groups, q, scale, mode, score) per signal, as dustin_srh_score_signals."""
+    arr, keep = _signal_array(signals, B)
+    n = _SZ(0)
+    _check(_signals_ws(B, n_max, len(signals), arr, ctypes.byref(n)), "dustin_srh_score_signals_workspace_size")
+    return n.value
+
+
+def dustin_srh_score_signals(ctx_len: torch.Tensor, signals, ws: torch.Tensor, stream=None):
+    """Both scoring signals in one call.  signals: (groups, q, scale, mode, score) per signal,
+    groups as in dustin_srh_score; every score [B][n_max] is written."""
+    _dev_i32(ctx_len, "ctx_len")
+    B = ctx_len.shape[0]
+    n_max = signals[0][4].shape[1]
+    arr, keep = _signal_array(signals, B)
+    _check(_signals(B, n_max, _ptr(ctx_len), len(signals), arr, _ptr(ws), ws.numel(), _stream(stream)),
+           "dustin_srh_score_signals")
 
 
 # ---------------------------------------------------------------------------- selection

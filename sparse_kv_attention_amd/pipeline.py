@@ -49,7 +49,11 @@ class SparseVerifyStep:
         mode_t = (D.SCORE_LOGIT_SUM_ALL if logit_sum_all else
                   D.SCORE_LOGIT_SUM2 if logit_sum2 else D.SCORE_PROB_SUM)
         self.mode_t = mode_t
-        ws_score = D.dustin_srh_score_workspace_size(B, n_max, nt, w.n_verify, mode_t)
+        self.scale_draft = 1.0 / math.sqrt(self.Dm.d)
+        self.scale = 1.0 / math.sqrt(self.T.d)
+        # both signals in one library call (one logit launch, one finalize)
+        ws_score = D.dustin_srh_score_signals_workspace_size(B, n_max, self.signals())
+        ws_score = max(ws_score, D.dustin_srh_score_workspace_size(B, n_max, nt, w.n_verify, mode_t))
         if self.has_draft:
             ws_score = max(ws_score, D.dustin_srh_score_workspace_size(B, n_max, nd, w.gamma, D.SCORE_PROB_SUM))
         self.ws_score = D.workspace(ws_score, dev)
@@ -65,13 +69,26 @@ class SparseVerifyStep:
             self.sel_params = (zeros, zeros, zeros)
         else:
             self.sel_params = (inp.n_sink, inp.n_window, inp.m)
-        self.scale_draft = 1.0 / math.sqrt(self.Dm.d)
-        self.scale = 1.0 / math.sqrt(self.T.d)
         self.out = torch.empty((B, w.n_verify, self.T.hq, self.T.d), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((B, self.T.hq, w.n_verify), dtype=torch.float32, device=dev)
 
     # ---- the stages ----
+    def signals(self):
+        """(groups, q, scale, mode, score) of the draft signal (when there is one) and the
+        target signal, with the current scales."""
+        inp = self.inp
+        sig = []
+        if self.has_draft:
+            sig.append((self.draft_groups, inp.q_srh_draft, self.scale_draft, D.SCORE_PROB_SUM, self.score_draft))
+        sig.append((self.target_groups, inp.q_srh_target, self.scale, self.mode_t, self.score_target))
+        return sig
+
     def score(self, stream=None):
+        """Both signals in one call."""
+        D.dustin_srh_score_signals(self.inp.ctx_len, self.signals(), self.ws_score, stream)
+
+    def score_separately(self, stream=None):
+        """The same scores from one call per signal."""
         inp = self.inp
         if self.has_draft:
             D.dustin_srh_score(inp.ctx_len, self.draft_groups, inp.q_srh_draft, self.scale_draft,

@@ -435,6 +435,40 @@ def test_scores_repeat_bitwise():
     say("  four scoring calls bitwise equal")
 
 
+def test_both_signals_in_one_call_match_separate_calls():
+    """dustin_srh_score_signals (one logit launch for the draft and target streams of
+    different head dims, one finalize) against one dustin_srh_score call per signal and
+    against the oracle, on a paged ragged workload and with the target in logit-sum mode."""
+    from sparse_kv_attention_amd import dustin as D
+    for name, w, kw in (("7B ragged", W.shrink(W.QWEN7B, batch=3, n_ctx=5000, ragged_lo=1000), {}),
+                        ("paged", W.shrink(W.RAGGED_PAGED, batch=2, n_ctx=3000, ragged_lo=700,
+                                           target=ModelShape(1, 64, 8, 128),
+                                           srh_target=((0, 0), (0, 8))), {}),
+                        ("collect-2 target", W.shrink(W.QWEN7B, batch=2, n_ctx=3000), {"logit_sum2": True})):
+        inp = W.make_inputs(w, device="cuda", target_layers=[0] if name != "paged" else None)
+        step = step_for(inp, [0], **kw)
+        bs = list(range(w.batch))
+        step.score()
+        torch.cuda.synchronize()
+        fused = (step.score_draft.clone(), step.score_target.clone())
+        step.score_draft.zero_()
+        step.score_target.zero_()
+        step.score_separately()
+        torch.cuda.synchronize()
+        sep = (step.score_draft.clone(), step.score_target.clone())
+        if kw:
+            cond = logit_abs_sum(inp, "target", bs)
+            check_scores(fused[1].cpu().numpy(), oracle_scores(inp, "target", O.LOGIT_SUM2, bs),
+                         f"{name}: target, one call", cond=cond)
+            check_scores(sep[1].cpu().numpy(), oracle_scores(inp, "target", O.LOGIT_SUM2, bs),
+                         f"{name}: target, own call", cond=cond)
+            continue
+        for i, sig in enumerate(("draft", "target")):
+            ora = oracle_scores(inp, sig, O.PROB_SUM, bs)
+            check_scores(fused[i].cpu().numpy(), ora, f"{name}: {sig}, one call")
+            check_scores(sep[i].cpu().numpy(), ora, f"{name}: {sig}, own call")
+
+
 def test_five_query_tiles():
     """72 query rows per KV head (G = 8, gamma = 8) fill five 16-row tiles in one workgroup:
     at head dim 128 the waves exchange their accumulators in two phases, at head dim 64 in
