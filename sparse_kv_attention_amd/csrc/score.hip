@@ -122,6 +122,9 @@ __device__ __forceinline__ void column_reduce_f32(float (&v)[N])
     }
 }
 
+// Pages of one workgroup's share the softmax-mode kernel resolves into LDS at its start.
+constexpr int kPageCache = 4096;
+
 // LDS bytes of one wave's staged tile at head dim D (row stride 2D + 16: conflict-free
 // 16-byte row reads)
 __host__ __device__ constexpr int prob_tile_bytes(int D) { return kStatTile * (2 * D + 16); }
@@ -132,7 +135,7 @@ __host__ __device__ constexpr int prob_tile_bytes(int D) { return kStatTile * (2
 // per-workgroup base plus token x stride (one 32x32->64 multiply-add per load).
 template <int D, bool FLAT>
 __device__ __forceinline__ void prob_logits(const ScoreArgs &a, const ScoreGroup &G, int b, int part, uint8_t *sK,
-                                            int &sNext)
+                                            int &sNext, int *sPage)
 {
     constexpr int NW = kProbWaves;
     constexpr int NT = 64 * NW;
@@ -183,9 +186,28 @@ __device__ __forceinline__ void prob_logits(const ScoreArgs &a, const ScoreGroup
         for (int ks = 0; ks < KS; ++ks)
             qop[ks] = qp ? load16(qp + ks * 32) : u32x4{0, 0, 0, 0};
     }
+    // Paged views: the pages of this workgroup's share, resolved once into LDS (clamped page
+    // ids), so a row's address needs no page-table load of its own; shares spanning more
+    // pages than the cache holds look each row's page up.  Rows past the share read row N-1
+    // through its own offset.
+    bool cached = false;
+    int pfirst = 0;
+    int64_t off_last = 0;
+    if constexpr (!FLAT) {
+        off_last = kv_offset(G.k, b, N - 1, G.kv_head);
+        if (G.k.pt) {
+            const int ps = G.k.ps_log2;
+            pfirst = (q_lo * kStatTile) >> ps;
+            const int plast = (min(q_hi * kStatTile, N) - 1) >> ps;
+            cached = plast - pfirst + 1 <= kPageCache;
+            if (cached)
+                for (int i = tid; i <= plast - pfirst; i += NT)
+                    sPage[i] = clampi(G.k.pt[(int64_t)b * G.k.max_pages + pfirst + i], 0, G.k.num_pages - 1);
+        }
+    }
     if (tid == 0)
         sNext = 0;
-    __syncthreads();                  // the tile counter ready
+    __syncthreads();                  // the tile counter and the page cache ready
     uint8_t *myK = sK + w * prob_tile_bytes(D);
 
     // A wave's tile is 64 tokens: lane l loads chunks l + 64 i (row = chunk / CPR) of the
@@ -208,10 +230,19 @@ __device__ __forceinline__ void prob_logits(const ScoreArgs &a, const ScoreGroup
             const int r = c / CPR;
             const int t = mine ? min(t0 + r, N - 1) : N - 1;
             const u32x4 *src;
-            if constexpr (FLAT)
+            if constexpr (FLAT) {
                 src = reinterpret_cast<const u32x4 *>(flat_base + (uint64_t)(uint32_t)t * flat_st);
-            else
-                src = reinterpret_cast<const u32x4 *>(G.k.base + kv_offset(G.k, b, t, G.kv_head) + (c - r * CPR) * 8);
+            } else {
+                int64_t off;
+                if (!mine || t0 + r >= N)
+                    off = off_last;
+                else if (cached)
+                    off = (int64_t)sPage[(t >> G.k.ps_log2) - pfirst] * G.k.sp +
+                          (int64_t)(t & ((1 << G.k.ps_log2) - 1)) * G.k.st + (int64_t)G.kv_head * G.k.sh;
+                else
+                    off = kv_offset(G.k, b, t, G.kv_head);
+                src = reinterpret_cast<const u32x4 *>(G.k.base + off + (c - r * CPR) * 8);
+            }
             kr[i] = __builtin_nontemporal_load(src);
         }
     };
@@ -367,6 +398,7 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
 {
     __shared__ __align__(16) uint8_t sK[kProbWaves * prob_tile_bytes(DM == 64 ? 64 : 128)];
     __shared__ int sNext;               // tiles claimed so far by the workgroup's waves
+    __shared__ int sPage[FLAT ? 1 : kPageCache];
     // workgroup -> (group, sequence, part): the groups' workgroups are consecutive ranges
     const int x = blockIdx.x;
     int gi = a.prob_g0;
@@ -377,14 +409,14 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
     const int b = r / G.parts;
     const int part = r - b * G.parts;
     if constexpr (DM == 64) {
-        prob_logits<64, FLAT>(a, G, b, part, sK, sNext);
+        prob_logits<64, FLAT>(a, G, b, part, sK, sNext, sPage);
     } else if constexpr (DM == 128) {
-        prob_logits<128, FLAT>(a, G, b, part, sK, sNext);
+        prob_logits<128, FLAT>(a, G, b, part, sK, sNext, sPage);
     } else {
         if (a.sig[G.sig].head_dim == 64)
-            prob_logits<64, FLAT>(a, G, b, part, sK, sNext);
+            prob_logits<64, FLAT>(a, G, b, part, sK, sNext, sPage);
         else
-            prob_logits<128, FLAT>(a, G, b, part, sK, sNext);
+            prob_logits<128, FLAT>(a, G, b, part, sK, sNext, sPage);
     }
 }
 
