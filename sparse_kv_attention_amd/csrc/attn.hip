@@ -53,10 +53,8 @@ constexpr float kLazy = 8.f;       // rescale O only when a tile's max exceeds t
 constexpr unsigned long long kCtrTag = 0xd5571a7e93ull << 24;
 constexpr unsigned long long kCtrTagMask = ~0ull << 24;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32)
@@ -101,14 +99,6 @@ __device__ __forceinline__ float max_over_quads(float x)
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// LDS transposing read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i receives
-// 16-bit element i % 4 of the 8-byte words addressed by lanes i / 4, 4 + i / 4, 8 + i / 4
-// and 12 + i / 4 of its group, in that order.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t *p)
-{
-    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
-    return __builtin_bit_cast(u32x2, v);
-}
 
 // LDS byte address of a pointer into the kernel's __shared__ array
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t *p)
@@ -126,7 +116,10 @@ __device__ __forceinline__ uint32_t xcc_id()
 // One ring step's MFMA operands out of LDS, in one inline-assembly block that ends with
 // its own wait (so every output is complete when the block ends): K as the A operand of
 // S^T = K Q^T (ka: 2 halves x KS k-steps, 16-byte reads) and V^T as the A operand of
-// O^T += V^T P^T (va: 2 halves x DVT head-dim tiles, transposing 8-byte reads).
+// O^T += V^T P^T (va: 2 halves x DVT head-dim tiles, transposing 8-byte reads).  The
+// transposing read (ds_read_b64_tr_b16): within each 16-lane group, lane i receives 16-bit
+// element i % 4 of the 8-byte words addressed by lanes i / 4, 4 + i / 4, 8 + i / 4 and
+// 12 + i / 4 of its group, in that order.
 __device__ __forceinline__ void read_step_ops(const uint32_t (&ka)[8], const uint32_t (&va)[16], u32x4 (&k)[8],
                                               u32x2 (&v)[16])
 {
@@ -641,6 +634,47 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
             issue(r, r);
         __builtin_amdgcn_sched_barrier(0);
     }
+    if (new_here) {
+        // the new-token step first: its rows were requested before the ring's first steps,
+        // which stay in flight (the wait counts exactly the ring loads issued after them)
+        const int issued = min(mine, R);
+        if (issued >= R)
+            wait_vmcnt<R * G::GOPS>();
+        else if (R > 3 && issued == 3)
+            wait_vmcnt<(R > 3 ? 3 : 0) * G::GOPS>();
+        else if (R > 2 && issued == 2)
+            wait_vmcnt<(R > 2 ? 2 : 0) * G::GOPS>();
+        else if (issued == 1)
+            wait_vmcnt<G::GOPS>();
+        else
+            wait_vmcnt<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        // rows 16..31 have zero operands and are masked.  The reads are one assembly block
+        // (the first half's addresses twice), so the compiler adds no wait for the ring
+        // loads still in flight.
+        const uint32_t na = lds_addr(nslot);
+        uint32_t ka[2 * G::KS], va[2 * G::DVT];
+#pragma unroll
+        for (int i = 0; i < 2 * G::KS; ++i)
+            ka[i] = na + kq[i % G::KS];
+#pragma unroll
+        for (int i = 0; i < 2 * G::DVT; ++i)
+            va[i] = na + vq[i % G::DVT] - G::HALF + 16 * G::RB;
+        u32x4 kraw[2 * G::KS];
+        u32x2 vraw[2 * G::DVT];
+        read_step_ops(ka, va, kraw, vraw);
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 kop[2][G::KS], vop[G::DVT];
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+            kop[0][ks] = kraw[ks];
+            kop[1][ks] = u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int dt = 0; dt < G::DVT; ++dt)
+            vop[dt] = u32x4{vraw[dt][0], vraw[dt][1], 0, 0};
+        math(kop, vop, false, nsel, true, nsel + a.nv);
+    }
     for (int j0 = 0; j0 < mine; j0 += R) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -686,23 +720,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
             math(kop, vop, pos0 + kTile <= p1, pos0, false, p1);
         }
     }
-    wait_vmcnt<0>();                  // the new-token rows have landed
-    if (new_here) {
-        // the new-token step: rows 16..31 have zero operands and are masked
-        u32x4 kop[2][G::KS];
-#pragma unroll
-        for (int ks = 0; ks < G::KS; ++ks) {
-            kop[0][ks] = *reinterpret_cast<const u32x4 *>(nslot + kq[ks]);
-            kop[1][ks] = u32x4{0, 0, 0, 0};
-        }
-        u32x4 vop[G::DVT];
-#pragma unroll
-        for (int dt = 0; dt < G::DVT; ++dt) {
-            const u32x2 v0 = lds_read_tr16(nslot + vq[dt] - G::HALF + 16 * G::RB);
-            vop[dt] = u32x4{v0[0], v0[1], 0, 0};
-        }
-        math(kop, vop, false, nsel, true, nsel + a.nv);
-    }
+    wait_vmcnt<0>();                  // every ring load of the wave has landed
 
     // ---- merge the four waves through LDS: every wave publishes its maxima, sums and
     //      O^T accumulators (all head-dim tiles, or half of them per phase), then wave w
