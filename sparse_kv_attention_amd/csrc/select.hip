@@ -279,15 +279,31 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a)
     for (int i = tid; i < kCopies * kHistStride; i += kSelectThreads)
         sh.hist[0][i] = 0;
     __syncthreads();
+    // the two tiers run the same code (one loop body): the selection code is fetched into
+    // the instruction cache once, not once per tier
     uint64_t selD = 0, selT = 0;
-    if (md > 0) {
-        to_keys<E>(key, valid);
-        selD = take_top<E>(key, valid & ~prot, md, sh);
-    }
-    if (r > 0) {
-        load_raw<E>(key, a.score_target + (int64_t)b * a.n_max, base, a.n_max);
-        to_keys<E>(key, valid);
-        selT = take_top<E>(key, valid & ~prot & ~selD, r, sh);
+#pragma unroll 1
+    for (int tier = 0; tier < 2; ++tier) {
+        const int kth = tier == 0 ? md : r;
+        if (kth <= 0)
+            continue;
+        // the thread's position and masks are made opaque to the compiler at the top of
+        // the body, so what is formed from them per key (addresses, mask tests) is formed
+        // in the loop rather than hoisted out of it and held, or spilled, through the tiers
+        int bs = base;
+        uint64_t vl = valid, pr = prot;
+        asm volatile("" : "+v"(bs), "+v"(vl), "+v"(pr));
+        if (tier == 1) {
+            const float *row = a.score_target + (int64_t)b * a.n_max;
+            asm volatile("" : "+s"(row));
+            load_raw<E>(key, row, bs, a.n_max);
+        }
+        to_keys<E>(key, vl);
+        const uint64_t sel = take_top<E>(key, vl & ~pr & ~selD, kth, sh);
+        if (tier == 0)
+            selD = sel;
+        else
+            selT = sel;
     }
     const uint64_t fin = prot | selD | selT;
     int total;
