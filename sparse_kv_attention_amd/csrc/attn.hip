@@ -212,12 +212,14 @@ struct AttnShape {
     static constexpr int RING = 4 * R * G::SLOT;
     static constexpr int TAB = 4 * kAttnStepsMaxW * kTile * 4;   // list entries / row numbers of the 4 waves
     static constexpr int NEWB = 2 * 16 * G::RB; // new-token rows: 16 K, then 16 V
-    // The four waves' accumulators are exchanged through the ring area in one pass, or in
-    // two (half of the head-dim tiles each) where one would not fit.
-    static constexpr int MRG1 = 4 * 64 * ACC * 4 + 2 * 4 * QR * 4;
-    static constexpr int PH = MRG1 > RING ? 2 : 1;
-    static constexpr int MRG = 4 * 64 * (ACC / PH) * 4 + 2 * 4 * QR * 4;
-    static_assert(MRG <= RING, "exchange fits the ring");
+    // The four waves' accumulators are exchanged through the ring area, each wave's through
+    // its own ring slots (free as soon as its own loop has ended), in one pass or in two
+    // (half of the head-dim tiles each) where one would not fit.
+    static constexpr int XW = RING / 4 / 4;     // floats of one wave's exchange area
+    static constexpr int MRG1 = 64 * ACC * 4 + 2 * QR * 4;
+    static constexpr int PH = MRG1 > RING / 4 ? 2 : 1;
+    static constexpr int MRG = 64 * (ACC / PH) * 4 + 2 * QR * 4;
+    static_assert(MRG <= RING / 4, "exchange fits a wave's ring slots");
     static constexpr int OFF_TAB = RING;
     static constexpr int OFF_NEW = OFF_TAB + TAB;
     static constexpr int OFF_FLAG = OFF_NEW + NEWB;
@@ -723,8 +725,9 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
     wait_vmcnt<0>();                  // every ring load of the wave has landed
 
     // ---- merge the four waves through LDS: every wave publishes its maxima, sums and
-    //      O^T accumulators (all head-dim tiles, or half of them per phase), then wave w
-    //      merges a quarter of the published tiles of every row ----
+    //      O^T accumulators (all head-dim tiles, or half of them per phase) into its own
+    //      ring slots as soon as its loop has ended (no wait for the other waves), then
+    //      wave w merges a quarter of the published tiles of every row ----
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
         lrun[qt] += __shfl_xor(lrun[qt], 16);
@@ -732,15 +735,17 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
     }
     constexpr int DVTP = G::DVT / S::PH;   // head-dim tiles exchanged per phase
     constexpr int DPW = DVTP / 4;          // head-dim tiles merged by each wave per phase
-    float *xAcc = reinterpret_cast<float *>(lds);              // [wave][dv tile of the phase][qt][lane][4]
-    float *xM = xAcc + 4 * 64 * (S::ACC / S::PH);               // [wave][QR]
-    float *xL = xM + 4 * S::QR;
-    __syncthreads();                  // every wave is done with its ring
+    // wave v's area: [dv tile of the phase][qt][lane][4] floats, then its maxima [QR] and
+    // sums [QR]
+    float *const xBase = reinterpret_cast<float *>(lds);
+    auto xAcc = [&](int v) { return xBase + v * S::XW; };
+    auto xM = [&](int v) { return xBase + v * S::XW + 64 * (S::ACC / S::PH); };
+    auto xL = [&](int v) { return xBase + v * S::XW + 64 * (S::ACC / S::PH) + S::QR; };
     if (quad == 0) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
-            xM[w * S::QR + qt * 16 + li] = mref[qt];
-            xL[w * S::QR + qt * 16 + li] = lrun[qt];
+            xM(w)[qt * 16 + li] = mref[qt];
+            xL(w)[qt * 16 + li] = lrun[qt];
         }
     }
     const bool direct_out = a.splits == 1;
@@ -757,22 +762,22 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
         for (int i = 0; i < DVTP; ++i)
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt)
-                *reinterpret_cast<f32x4 *>(xAcc + (((w * DVTP + i) * QT + qt) * 64 + lane) * 4) = acc[ph * DVTP + i][qt];
-        __syncthreads();
+                *reinterpret_cast<f32x4 *>(xAcc(w) + ((i * QT + qt) * 64 + lane) * 4) = acc[ph * DVTP + i][qt];
+        __syncthreads();              // every wave's tiles, maxima and sums are published
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
             const int q = qt * 16 + li;
             float mw[4], M = -INFINITY;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                mw[v] = xM[v * S::QR + q];
+                mw[v] = xM(v)[q];
                 M = fmaxf(M, mw[v]);
             }
             float f[4], l = 0.f;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 f[v] = M == -INFINITY ? 0.f : fast_exp2(mw[v] - M);
-                l += f[v] * xL[v * S::QR + q];
+                l += f[v] * xL(v)[q];
             }
             resM[qt] = M;
             resL[qt] = l;
@@ -782,7 +787,7 @@ __global__ __launch_bounds__(kThreads) void verify_attn_kernel(AttnArgs a)
                 f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    o += f[v] * *reinterpret_cast<const f32x4 *>(xAcc + (((v * DVTP + i) * QT + qt) * 64 + lane) * 4);
+                    o += f[v] * *reinterpret_cast<const f32x4 *>(xAcc(v) + ((i * QT + qt) * 64 + lane) * 4);
                 res[ph][qt][j] = o;
             }
         }
