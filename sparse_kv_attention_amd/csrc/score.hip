@@ -399,8 +399,34 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
     __shared__ __align__(16) uint8_t sK[kProbWaves * prob_tile_bytes(DM == 64 ? 64 : 128)];
     __shared__ int sNext;               // tiles claimed so far by the workgroup's waves
     __shared__ int sPage[FLAT ? 1 : kPageCache];
-    // workgroup -> (group, sequence, part): the groups' workgroups are consecutive ranges
     const int x = blockIdx.x;
+    auto run = [&](const ScoreGroup &G, int b, int part) {
+        if constexpr (DM == 64) {
+            prob_logits<64, FLAT>(a, G, b, part, sK, sNext, sPage);
+        } else if constexpr (DM == 128) {
+            prob_logits<128, FLAT>(a, G, b, part, sK, sNext, sPage);
+        } else {
+            if (a.sig[G.sig].head_dim == 64)
+                prob_logits<64, FLAT>(a, G, b, part, sK, sNext, sPage);
+            else
+                prob_logits<128, FLAT>(a, G, b, part, sK, sNext, sPage);
+        }
+    };
+    if (a.paired) {
+        // workgroup -> (pair i, sequence, part): one share of group i of the first half, then
+        // the same share of group i of the second half (every group has the same parts)
+        const int half = a.prob_ng / 2;
+        const ScoreGroup &G0 = a.grp[a.prob_g0];
+        const int per = a.B * G0.parts;
+        const int i = x / per;
+        const int b = (x - i * per) / G0.parts;
+        const int part = x - i * per - b * G0.parts;
+        run(a.grp[a.prob_g0 + i], b, part);
+        __syncthreads();              // the LDS areas and the tile counter are free again
+        run(a.grp[a.prob_g0 + half + i], b, part);
+        return;
+    }
+    // workgroup -> (group, sequence, part): the groups' workgroups are consecutive ranges
     int gi = a.prob_g0;
     for (int g = a.prob_g0 + 1; g < a.prob_g0 + a.prob_ng; ++g)
         gi = x >= a.grp[g].wg0 ? g : gi;
@@ -408,16 +434,7 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
     const int r = x - G.wg0;
     const int b = r / G.parts;
     const int part = r - b * G.parts;
-    if constexpr (DM == 64) {
-        prob_logits<64, FLAT>(a, G, b, part, sK, sNext, sPage);
-    } else if constexpr (DM == 128) {
-        prob_logits<128, FLAT>(a, G, b, part, sK, sNext, sPage);
-    } else {
-        if (a.sig[G.sig].head_dim == 64)
-            prob_logits<64, FLAT>(a, G, b, part, sK, sNext, sPage);
-        else
-            prob_logits<128, FLAT>(a, G, b, part, sK, sNext, sPage);
-    }
+    run(G, b, part);
 }
 
 // ---- logit-sum mode: raw scaled logits on MFMA -------------------------------------
@@ -658,6 +675,35 @@ hipError_t launch_prob_variant(ScoreArgs &a, int cus, hipStream_t st)
     // one resident round of workgroups, shared among the groups in proportion to their
     // bytes per token (the head dim), at least one and at most the workspace's count each
     const int slots = std::max(1, per_cu * cus / std::max(1, a.B));
+    // Two signals with the same number of groups and different head dims (the draft's and
+    // the target's): whole parts per group cannot match bytes per workgroup (64 against
+    // 128 would need 2.67 and 5.33 shares of 32), so every workgroup takes the same share
+    // of one group of each, and every workgroup moves the same bytes.
+    a.paired = 0;
+    if (DM == 0 && a.prob_ng % 2 == 0) {
+        const int half = a.prob_ng / 2;
+        const int parts = std::min(a.n_parts, slots / half);
+        bool ok = parts >= 1;
+        for (int i = 0; i < half && ok; ++i) {
+            const ScoreGroup &A = a.grp[a.prob_g0 + i], &Bg = a.grp[a.prob_g0 + half + i];
+            ok = a.sig[A.sig].head_dim == a.sig[a.grp[a.prob_g0].sig].head_dim &&
+                 a.sig[Bg.sig].head_dim == a.sig[a.grp[a.prob_g0 + half].sig].head_dim &&
+                 a.sig[A.sig].head_dim != a.sig[Bg.sig].head_dim;
+        }
+        if (ok) {
+            int wg = 0;
+            for (int g = a.prob_g0; g < a.prob_g0 + a.prob_ng; ++g) {
+                a.grp[g].parts = parts;
+                a.grp[g].wg0 = g < a.prob_g0 + half ? wg : a.grp[g - half].wg0;
+                if (g < a.prob_g0 + half)
+                    wg += parts * a.B;
+            }
+            a.n_parts = parts;
+            a.paired = 1;
+            hipLaunchKernelGGL((srh_prob_logits_kernel<DM, FLAT>), dim3((unsigned)wg), dim3(nt), 0, st, a);
+            return hipGetLastError();
+        }
+    }
     int dsum = 0;
     for (int g = a.prob_g0; g < a.prob_g0 + a.prob_ng; ++g)
         dsum += a.sig[a.grp[g].sig].head_dim;
