@@ -93,9 +93,6 @@ constexpr int kMaxSignals = 2;
 struct ScoreArgs {
     int B, n_max, n_pad, n_tiles, n_parts, n_sig;
     int prob_g0, prob_ng;    // the softmax-mode launch covers grp[prob_g0 .. prob_g0 + prob_ng)
-    int paired;              // softmax-mode workgroups take one share of group i of the first
-                             //   half and one of group i of the second (equal bytes per
-                             //   workgroup when the halves' head dims differ)
     const int32_t *ctx_len;
     ScoreSig sig[kMaxSignals];
     ScoreGroup grp[kMaxGroups];

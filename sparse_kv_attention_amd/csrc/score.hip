@@ -390,6 +390,24 @@ __device__ __forceinline__ void prob_logits(const ScoreArgs &a, const ScoreGroup
 }
 
 
+// One workgroup's share of group G, on the path of the group's head dim (DM: the head dim
+// of every group launched, or 0 when both occur).
+template <int DM, bool FLAT>
+__device__ __forceinline__ void prob_group(const ScoreArgs &a, const ScoreGroup &G, int b, int part, uint8_t *sK,
+                                           int &sNext, int *sPage)
+{
+    if constexpr (DM == 64) {
+        prob_logits<64, FLAT>(a, G, b, part, sK, sNext, sPage);
+    } else if constexpr (DM == 128) {
+        prob_logits<128, FLAT>(a, G, b, part, sK, sNext, sPage);
+    } else {
+        if (a.sig[G.sig].head_dim == 64)
+            prob_logits<64, FLAT>(a, G, b, part, sK, sNext, sPage);
+        else
+            prob_logits<128, FLAT>(a, G, b, part, sK, sNext, sPage);
+    }
+}
+
 // DM: the head dim of every group launched (64 or 128), or 0 when the launch holds groups
 // of both head dims (each workgroup then takes its group's path; the LDS is sized for 128).
 template <int DM, bool FLAT>
@@ -400,32 +418,6 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
     __shared__ int sNext;               // tiles claimed so far by the workgroup's waves
     __shared__ int sPage[FLAT ? 1 : kPageCache];
     const int x = blockIdx.x;
-    auto run = [&](const ScoreGroup &G, int b, int part) {
-        if constexpr (DM == 64) {
-            prob_logits<64, FLAT>(a, G, b, part, sK, sNext, sPage);
-        } else if constexpr (DM == 128) {
-            prob_logits<128, FLAT>(a, G, b, part, sK, sNext, sPage);
-        } else {
-            if (a.sig[G.sig].head_dim == 64)
-                prob_logits<64, FLAT>(a, G, b, part, sK, sNext, sPage);
-            else
-                prob_logits<128, FLAT>(a, G, b, part, sK, sNext, sPage);
-        }
-    };
-    if (a.paired) {
-        // workgroup -> (pair i, sequence, part): one share of group i of the first half, then
-        // the same share of group i of the second half (every group has the same parts)
-        const int half = a.prob_ng / 2;
-        const ScoreGroup &G0 = a.grp[a.prob_g0];
-        const int per = a.B * G0.parts;
-        const int i = x / per;
-        const int b = (x - i * per) / G0.parts;
-        const int part = x - i * per - b * G0.parts;
-        run(a.grp[a.prob_g0 + i], b, part);
-        __syncthreads();              // the LDS areas and the tile counter are free again
-        run(a.grp[a.prob_g0 + half + i], b, part);
-        return;
-    }
     // workgroup -> (group, sequence, part): the groups' workgroups are consecutive ranges
     int gi = a.prob_g0;
     for (int g = a.prob_g0 + 1; g < a.prob_g0 + a.prob_ng; ++g)
@@ -434,7 +426,32 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_logits_kernel
     const int r = x - G.wg0;
     const int b = r / G.parts;
     const int part = r - b * G.parts;
-    run(G, b, part);
+    prob_group<DM, FLAT>(a, G, b, part, sK, sNext, sPage);
+}
+
+// The softmax-mode kernel when the launch pairs the groups of two signals (head dims D1
+// for the first half of the groups, D2 for the second, D1 != D2): workgroup -> (pair i,
+// sequence, part), one share of group i of the first half, then the same share of group i
+// of the second half (every group has the same parts), so every workgroup moves the same
+// bytes.  A kernel of its own: with both paths in one kernel, the tile arrays of its four
+// inlined copies ended up in scratch memory.
+template <int D1, int D2, bool FLAT>
+__global__ __launch_bounds__(64 * kProbWaves)
+__attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_pair_kernel(ScoreArgs a)
+{
+    __shared__ __align__(16) uint8_t sK[kProbWaves * prob_tile_bytes(D1 > D2 ? D1 : D2)];
+    __shared__ int sNext;
+    __shared__ int sPage[FLAT ? 1 : kPageCache];
+    const int x = blockIdx.x;
+    const int half = a.prob_ng / 2;
+    const ScoreGroup &G0 = a.grp[a.prob_g0];
+    const int per = a.B * G0.parts;
+    const int i = x / per;
+    const int b = (x - i * per) / G0.parts;
+    const int part = x - i * per - b * G0.parts;
+    prob_logits<D1, FLAT>(a, a.grp[a.prob_g0 + i], b, part, sK, sNext, sPage);
+    __syncthreads();                  // the LDS areas and the tile counter are free again
+    prob_logits<D2, FLAT>(a, a.grp[a.prob_g0 + half + i], b, part, sK, sNext, sPage);
 }
 
 // ---- logit-sum mode: raw scaled logits on MFMA -------------------------------------
@@ -679,7 +696,6 @@ hipError_t launch_prob_variant(ScoreArgs &a, int cus, hipStream_t st)
     // the target's): whole parts per group cannot match bytes per workgroup (64 against
     // 128 would need 2.67 and 5.33 shares of 32), so every workgroup takes the same share
     // of one group of each, and every workgroup moves the same bytes.
-    a.paired = 0;
     if (DM == 0 && a.prob_ng % 2 == 0) {
         const int half = a.prob_ng / 2;
         const int parts = std::min(a.n_parts, slots / half);
@@ -699,8 +715,10 @@ hipError_t launch_prob_variant(ScoreArgs &a, int cus, hipStream_t st)
                     wg += parts * a.B;
             }
             a.n_parts = parts;
-            a.paired = 1;
-            hipLaunchKernelGGL((srh_prob_logits_kernel<DM, FLAT>), dim3((unsigned)wg), dim3(nt), 0, st, a);
+            if (a.sig[a.grp[a.prob_g0].sig].head_dim == 64)
+                hipLaunchKernelGGL((srh_prob_pair_kernel<64, 128, FLAT>), dim3((unsigned)wg), dim3(nt), 0, st, a);
+            else
+                hipLaunchKernelGGL((srh_prob_pair_kernel<128, 64, FLAT>), dim3((unsigned)wg), dim3(nt), 0, st, a);
             return hipGetLastError();
         }
     }
