@@ -180,7 +180,16 @@ dustin_status dustin_srh_score_signals(int B, int n_max, const int32_t *ctx_len,
  *   count : int32 [B] = |I|
  *   budget, n_sink, n_window, m : int32 [B] (negative values act as 0)
  *   score_draft, score_target : fp32 [B][n_max], 16-byte aligned (else INVALID_ARG)
- *   n_max <= 65536.  workspace: dustin_select_workspace_size(...) bytes (may be 0).
+ *   n_max <= 65536.
+ *   workspace: NULL, or dustin_select_workspace_size(...) bytes (B x (16 KiB + 8)),
+ *   16-byte aligned, any contents on the first call (else DUSTIN_ERR_WORKSPACE).  With a
+ *   workspace, a sequence whose two tiers are both non-empty (and |D| + |T| <= 4096) runs
+ *   them on two workgroups at once: the best |T| of the best |D| + |T| candidates by
+ *   score_target that are not in D are exactly T.  Each workgroup publishes its tier's
+ *   position mask and counts itself in on the sequence's arrival counter (recognised by
+ *   a 40-bit tag, left cleared by the call); the second to arrive combines the two.
+ *   Without a workspace, one workgroup runs both tiers in turn; the result is the same
+ *   set either way.
  * ------------------------------------------------------------------------------- */
 dustin_status dustin_select_workspace_size(int B, int n_max, size_t *bytes /* host */);
 dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const float *score_draft,

@@ -504,7 +504,8 @@ dustin_status dustin_select_workspace_size(int B, int n_max, size_t *bytes)
 {
     if (!bytes || B < 0 || n_max < 0)
         return DUSTIN_ERR_INVALID_ARG;
-    *bytes = 0;
+    // the two tiers' chosen-position masks and an arrival counter for every sequence
+    *bytes = select_ws_bytes(B);
     return DUSTIN_OK;
 }
 
@@ -514,8 +515,6 @@ dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const floa
                             int k_max, int32_t *idx, int32_t *count, void *workspace,
                             size_t workspace_bytes, void *stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     if (B < 0 || n_max < 0 || k_max < 0)
         return DUSTIN_ERR_INVALID_ARG;
     if (n_max > kSelectMaxN)
@@ -528,6 +527,9 @@ dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const floa
     // the kernels read score rows as 16-byte vectors
     if (!aligned16(score_target) || (score_draft && !aligned16(score_draft)))
         return DUSTIN_ERR_INVALID_ARG;
+    // no workspace: one workgroup per sequence runs both tiers in turn
+    if (workspace && (workspace_bytes < select_ws_bytes(B) || !aligned16(workspace)))
+        return DUSTIN_ERR_WORKSPACE;
     SelectArgs a;
     a.B = B;
     a.n_max = n_max;
@@ -541,6 +543,7 @@ dustin_status dustin_select(int B, int n_max, const int32_t *ctx_len, const floa
     a.m = m;
     a.idx = idx;
     a.count = count;
+    a.ws = static_cast<unsigned long long *>(workspace);
     const hipError_t e = launch_select(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
 }

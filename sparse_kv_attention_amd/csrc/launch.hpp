@@ -112,7 +112,17 @@ struct SelectArgs {
     const float *score_target;
     const int32_t *budget, *n_sink, *n_window, *m;
     int32_t *idx, *count;
+    unsigned long long *ws;     // [B][2][kSelectThreads] chosen-position masks of the two tiers,
+                                //   then [B] arrival counters (nullptr: one workgroup per
+                                //   sequence runs both tiers)
 };
+constexpr int kSelectCombineCap = 4096;   // r + m up to which the tiers run on two workgroups
+
+// bytes of the selection workspace for B sequences: the masks and the counters
+inline size_t select_ws_bytes(int B)
+{
+    return (size_t)B * (2 * kSelectThreads + 1) * sizeof(unsigned long long);
+}
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t st);
 

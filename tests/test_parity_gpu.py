@@ -528,6 +528,46 @@ def test_selection_stops_early_on_a_whole_digit_bin():
     say("  early stops after passes 1, 2, 3 and the all-ties case bit-exact")
 
 
+def test_selection_two_workgroups_match_one():
+    """With a workspace, a sequence whose two tiers are both non-empty (|D| + |T| <= 4096)
+    runs them on two workgroups, the second to finish combining them; without one, one
+    workgroup runs both in turn.  Both must give the oracle's set bit for bit: ragged
+    contexts at 32 and 64 keys per thread, nine sequences (a second, partial group of
+    eight), ties (quantised scores) in the tiers and in the combined candidates, candidate
+    lists of up to 2 and up to 4 per thread, a sequence above the 4096 cap, one with
+    m = 0, one with the budget at least the context, one whose draft tier fills the
+    budget, and a workspace that starts with random bytes."""
+    from sparse_kv_attention_amd import dustin as D
+    B, n_max, k_max = 9, 40000, 5000
+    ctx = np.array([32768, 40000, 30001, 12000, 500, 20000, 32768, 40000, 39999], dtype=np.int32)
+    budget = np.array([2048, 2048, 1777, 2900, 600, 1024, 2048, 4800, 4000], dtype=np.int32)
+    sink = np.array([16, 16, 3, 16, 4, 16, 16, 16, 16], dtype=np.int32)
+    window = np.array([256, 256, 40, 256, 8, 128, 256, 256, 100], dtype=np.int32)
+    m = np.array([768, 768, 1000, 768, 100, 0, 2000, 768, 1500], dtype=np.int32)
+    gen = np.random.default_rng(77)
+    sd = gen.uniform(0, 1e-3, (B, n_max)).astype(np.float32)
+    st = gen.uniform(0, 1e-3, (B, n_max)).astype(np.float32)
+    sd[2] = np.round(sd[2] * 3000) / 3000
+    st[2] = np.round(st[2] * 3000) / 3000
+    st[8] = np.round(st[8] * 5e5) / 5e5          # ties among the combined candidates
+    want_idx, want_cnt = O.select(ctx, sd, st, budget, sink, window, m, k_max)
+    dev = "cuda"
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    ws = D.workspace(D.dustin_select_workspace_size(B, n_max), dev)
+    ws.copy_(torch.from_numpy(gen.integers(0, 256, ws.numel(), dtype=np.uint8)).to(dev))
+    got = {}
+    for name, w in (("two workgroups", ws), ("one workgroup", None), ("two workgroups again", ws)):
+        idx = torch.full((B, k_max), -5, dtype=torch.int32, device=dev)
+        cnt = torch.zeros((B,), dtype=torch.int32, device=dev)
+        D.dustin_select(t(ctx), t(sd), t(st), t(budget), t(sink), t(window), t(m), idx, cnt, w)
+        torch.cuda.synchronize()
+        assert np.array_equal(cnt.cpu().numpy(), want_cnt), name
+        got[name] = idx.cpu().numpy()
+        for b in range(B):
+            assert np.array_equal(got[name][b], want_idx[b]), f"{name}: sequence {b}"
+    say("  two-workgroup and one-workgroup selection identical to the oracle")
+
+
 def test_context_above_32k():
     """Contexts of 30k..50k tokens (ragged): 64 keys per selection thread (the widest
     selection variant), scoring over 50k-token rows, a 4096-token budget over two splits
