@@ -96,6 +96,31 @@ __device__ __forceinline__ double wave_max_f64_dpp(double v)
     return swap_max_f64(v, true);
 }
 
+__device__ __forceinline__ double swap_add_f64(double v, bool wide)
+{
+    const uint64_t u = __double_as_longlong(v);
+    const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    const auto a = wide ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                        : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = wide ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                        : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const double x = __longlong_as_double((long long)(((uint64_t)b[0] << 32) | a[0]));
+    const double y = __longlong_as_double((long long)(((uint64_t)b[1] << 32) | a[1]));
+    return x + y;
+}
+
+// Sum over the 64 lanes, every lane ending with it: the same exchange pattern as
+// wave_max_f64_dpp (pairs, quads, half rows, rows, then the row and half swaps).
+__device__ __forceinline__ double wave_sum_f64_dpp(double v)
+{
+    v += dpp64<0xB1>(v);
+    v += dpp64<0x4E>(v);
+    v += dpp64<0x141>(v);
+    v += dpp64<0x140>(v);
+    v = swap_add_f64(v, false);
+    return swap_add_f64(v, true);
+}
+
 // Waves per workgroup of the softmax-mode logit kernel: two per SIMD.  One workgroup
 // fills a CU, so all of a CU's waves draw tiles from one counter and none is left running
 // alone at the end.
@@ -164,10 +189,14 @@ __device__ __forceinline__ void prob_logits(const ScoreArgs &a, const ScoreGroup
             S.tile_max[e] = -INFINITY;
         }
     if (q_lo >= q_hi) {
+        // the empty partial in this workgroup's slot and the slots past the group's
+        // workgroups that it covers
         for (int p = tid; p < G.n_pairs; p += NT) {
-            const int64_t e = ((int64_t)b * S.total_pairs + G.pair0 + p) * a.n_parts + part;
-            S.part_max[e] = -INFINITY;
-            S.part_sum[e] = 0.0;
+            const int64_t e = ((int64_t)b * S.total_pairs + G.pair0 + p) * a.n_parts;
+            for (int x = part; x < a.n_parts; x += G.parts) {
+                S.part_max[e + x] = -INFINITY;
+                S.part_sum[e + x] = 0.0;
+            }
         }
         return;
     }
@@ -377,14 +406,17 @@ __device__ __forceinline__ void prob_logits(const ScoreArgs &a, const ScoreGroup
             }
         }
         const double M = wave_max_f64_dpp(Ml);
-        double Z = Ml > -INFINITY ? Sl * (double)fast_exp2((float)(Ml - M)) : 0.0;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1)
-            Z += __shfl_xor(Z, o);
+        const double Z = wave_sum_f64_dpp(Ml > -INFINITY ? Sl * (double)fast_exp2((float)(Ml - M)) : 0.0);
         if (lane == 0) {
-            const int64_t e = ((int64_t)b * S.total_pairs + G.pair0 + p) * a.n_parts + part;
-            S.part_max[e] = M;
-            S.part_sum[e] = Z;
+            const int64_t e = ((int64_t)b * S.total_pairs + G.pair0 + p) * a.n_parts;
+            S.part_max[e + part] = M;
+            S.part_sum[e + part] = Z;
+            // the record's slots beyond the group's workgroups hold the empty partial, so
+            // the finalize folds every slot without knowing the group's count
+            for (int x = G.parts + part; x < a.n_parts; x += G.parts) {
+                S.part_max[e + x] = -INFINITY;
+                S.part_sum[e + x] = 0.0;
+            }
         }
     }
 }
@@ -554,7 +586,7 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a, in
 
 constexpr int kFinTokens = 1024;          // = kThreads * 4: every thread sums four tokens
 constexpr int kFinTiles = kFinTokens / kStatTile;
-constexpr int kFinBatch = 8;               // pairs per wave whose statistics loads are in flight together
+constexpr int kFinBatch = 5;               // pairs per wave whose statistics loads are in flight together
 constexpr int kFinChunk = 32;              // pairs whose logits one finalize thread holds at once
 
 __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
@@ -568,60 +600,87 @@ __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
     const int N = clampi(a.ctx_len[b], 0, S.ctx_clamp);
     const bool prob = S.mode == DUSTIN_SCORE_PROB_SUM;
     const int tile0 = blockIdx.x * kFinTiles;
-    // this thread's 4 tokens: the logits of the first kFinChunk pairs are requested before
-    // the statistics (which do not need them), all in one round of loads
+    // this thread's 4 tokens: the statistics of the wave's first kFinBatch pairs are
+    // requested first and the logits of the first kFinChunk pairs right behind them, all
+    // as unconditional loads at clamped addresses (values outside the ranges are replaced
+    // after the loads), so the statistics can be reduced while the logits are in flight
     const int P = prob ? S.total_pairs : S.n_groups;   // logit rows summed per token
     const int tb = blockIdx.x * kFinTokens + tid * 4;
     const bool live = tb < N;
-    const float *lg = S.logits + (int64_t)b * S.logit_rows * a.n_pad + tb;
+    const float *lg = S.logits + (int64_t)b * S.logit_rows * a.n_pad + (live ? tb : 0);
+    const int p_last = max(P - 1, 0);
     f32x4 lv[kFinChunk];
     auto fetch = [&](int p0) {
 #pragma unroll
-        for (int j = 0; j < kFinChunk; ++j) {
-            const int p = min(p0 + j, P - 1);
-            lv[j] = live ? *reinterpret_cast<const f32x4 *>(lg + (int64_t)p * a.n_pad) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int j = 0; j < kFinChunk; ++j)
+            lv[j] = *reinterpret_cast<const f32x4 *>(lg + (int64_t)min(p0 + j, p_last) * a.n_pad);
     };
-    fetch(0);
     if (prob) {
-        // one wave per pair, kFinBatch pairs at a time with all their loads issued together:
-        // lanes take the workgroup partials (at most kScoreParts) for the pair's max (fp64)
-        // and normaliser (fp32 exp2 of the fp64 difference, summed in fp64), and lanes below
-        // kFinTiles the maxima of this block's statistics tiles
+        // one wave per pair, kFinBatch pairs at a time: lanes take the workgroup partials
+        // (at most kScoreParts) for the pair's max (fp64) and normaliser (fp32 exp2 of the
+        // fp64 difference, summed in fp64), and lanes below kFinTiles the maxima of this
+        // block's statistics tiles
         const int w = tid >> 6, lane = tid & 63;
-        const int t = tile0 + lane;
-        for (int p0 = w; p0 < S.total_pairs; p0 += 4 * kFinBatch) {
-            double pm[kFinBatch], ps[kFinBatch], tm[kFinBatch];
+        const int tc = min(tile0 + min(lane, kFinTiles - 1), a.n_tiles - 1);   // lanes past the block's tiles repeat its last
+        const int pi = min(lane, max(a.n_parts, 1) - 1);
+        const int row_last = max(S.total_pairs - 1, 0);
+        double pm[kFinBatch], ps[kFinBatch], tm[kFinBatch];
+        auto load_stats = [&](int p0) {
+            // every slot of the pair's record (slots past its group's workgroups hold the
+            // empty partial)
 #pragma unroll
             for (int k = 0; k < kFinBatch; ++k) {
-                const int p = p0 + 4 * k;
-                const int64_t row = (int64_t)b * S.total_pairs + p;
-                const bool ok = p < S.total_pairs;
-                // the workgroups that shared the tiles of the pair's group
-                int np = 1;
-                for (int g = S.g0; g < S.g0 + S.n_groups; ++g)
-                    np = p >= a.grp[g].pair0 ? a.grp[g].parts : np;
-                pm[k] = ok && lane < np ? S.part_max[row * a.n_parts + lane] : -INFINITY;
-                ps[k] = ok && lane < np ? S.part_sum[row * a.n_parts + lane] : 0.0;
-                tm[k] = ok && lane < kFinTiles && t < a.n_tiles ? S.tile_max[row * a.n_tiles + t] : -INFINITY;
+                const int64_t row = (int64_t)b * S.total_pairs + min(p0 + 4 * k, row_last);
+                pm[k] = S.part_max[row * a.n_parts + pi];
+                ps[k] = S.part_sum[row * a.n_parts + pi];
+                tm[k] = S.tile_max[row * a.n_tiles + tc];
+            }
+        };
+        auto reduce_stats = [&](int p0) {
+            // the batch's pairs in three branch-free passes (their reduction chains
+            // interleave), then the stores
+            double M[kFinBatch], Z[kFinBatch];
+#pragma unroll
+            for (int k = 0; k < kFinBatch; ++k) {
+                const bool ok = p0 + 4 * k < S.total_pairs && lane < a.n_parts;
+                pm[k] = ok ? pm[k] : -INFINITY;
+                ps[k] = ok ? ps[k] : 0.0;
+                M[k] = wave_max_f64_dpp(pm[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < kFinBatch; ++k)
+                Z[k] = wave_sum_f64_dpp(ps[k] > 0.0 ? ps[k] * (double)fast_exp2((float)(pm[k] - M[k])) : 0.0);
+            float iz[kFinBatch], off[kFinBatch];
+#pragma unroll
+            for (int k = 0; k < kFinBatch; ++k) {
+                const bool tok = lane < kFinTiles && tile0 + lane < a.n_tiles && tm[k] > -INFINITY;
+                iz[k] = Z[k] > 0.0 ? (float)(1.0 / Z[k]) : 0.f;
+                off[k] = tok ? (float)(tm[k] - M[k]) : 0.f;
             }
 #pragma unroll
             for (int k = 0; k < kFinBatch; ++k) {
                 const int p = p0 + 4 * k;
-                const double M = wave_max_f64_dpp(pm[k]);
-                double Z = ps[k] > 0.0 ? ps[k] * (double)fast_exp2((float)(pm[k] - M)) : 0.0;
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1)
-                    Z += __shfl_xor(Z, o);
                 if (p < S.total_pairs) {
                     if (lane == 0)
-                        sInvZ[p] = Z > 0.0 ? (float)(1.0 / Z) : 0.f;
+                        sInvZ[p] = iz[k];
                     if (lane < kFinTiles)
-                        sOff[p][lane] = tm[k] > -INFINITY ? (float)(tm[k] - M) : 0.f;
+                        sOff[p][lane] = off[k];
                 }
             }
+        };
+        // the first batch with the logits requested right behind its statistics (no branch
+        // between them, so the wait for the statistics leaves the logits in flight)
+        load_stats(w);
+        fetch(0);
+        __builtin_amdgcn_sched_barrier(0);   // every load issued before the first wait
+        reduce_stats(w);
+        for (int p0 = w + 4 * kFinBatch; p0 < S.total_pairs; p0 += 4 * kFinBatch) {
+            load_stats(p0);
+            reduce_stats(p0);
         }
         __syncthreads();
+    } else {
+        fetch(0);
     }
     if (tb >= a.n_max)
         return;
