@@ -587,7 +587,7 @@ __global__ __launch_bounds__(kThreads) void srh_logit_sum_kernel(ScoreArgs a, in
 constexpr int kFinTokens = 1024;          // = kThreads * 4: every thread sums four tokens
 constexpr int kFinTiles = kFinTokens / kStatTile;
 constexpr int kFinBatch = 5;               // pairs per wave whose statistics loads are in flight together
-constexpr int kFinChunk = 32;              // pairs whose logits one finalize thread holds at once
+constexpr int kFinChunk = 20;              // pairs whose logits one finalize thread holds at once (rows past a signal's last repeat it)
 
 __global__ __launch_bounds__(kThreads) void srh_finalize_kernel(ScoreArgs a)
 {
