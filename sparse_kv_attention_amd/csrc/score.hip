@@ -158,9 +158,15 @@ __host__ __device__ constexpr int prob_tile_bytes(int D) { return kStatTile * (2
 // tile areas (kProbWaves x prob_tile_bytes(D)); sNext: the workgroup's tile counter.
 // FLAT: every group's view is unpaged with a row stride below 4 GiB, so a row address is a
 // per-workgroup base plus token x stride (one 32x32->64 multiply-add per load).
+// setup: zero the tile counter (and fill the page cache) behind a workgroup barrier; a
+// caller that zeroed the counter at kernel start passes false (unpaged views only).
+// wave_bytes: the stride of the waves' LDS areas (at least prob_tile_bytes(D)).  sDone:
+// nullptr, or a zeroed LDS counter of the waves done with the group: then no barrier ends
+// the group, and the last wave to finish folds it alone while the others go on.
 template <int D, bool FLAT>
 __device__ __forceinline__ void prob_logits(const ScoreArgs &a, const ScoreGroup &G, int b, int part, uint8_t *sK,
-                                            int &sNext, int *sPage)
+                                            int &sNext, int *sPage, bool setup = true,
+                                            int wave_bytes = prob_tile_bytes(D), int *sDone = nullptr)
 {
     constexpr int NW = kProbWaves;
     constexpr int NT = 64 * NW;
@@ -234,10 +240,12 @@ __device__ __forceinline__ void prob_logits(const ScoreArgs &a, const ScoreGroup
                     sPage[i] = clampi(G.k.pt[(int64_t)b * G.k.max_pages + pfirst + i], 0, G.k.num_pages - 1);
         }
     }
-    if (tid == 0)
-        sNext = 0;
-    __syncthreads();                  // the tile counter and the page cache ready
-    uint8_t *myK = sK + w * prob_tile_bytes(D);
+    if (setup) {
+        if (tid == 0)
+            sNext = 0;
+        __syncthreads();              // the tile counter and the page cache ready
+    }
+    uint8_t *myK = sK + w * wave_bytes;
 
     // A wave's tile is 64 tokens: lane l loads chunks l + 64 i (row = chunk / CPR) of the
     // tile's rows (whole rows per instruction: the coalescing the matrix-core operand
@@ -390,10 +398,25 @@ __device__ __forceinline__ void prob_logits(const ScoreArgs &a, const ScoreGroup
     }
     // This workgroup's (max, sum of exp2(l - max)) per pair over its tiles, folded in a
     // fixed order whichever wave took a tile, so the result does not depend on the claims:
-    // one wave per pair, lane i folding tiles q_lo + i, q_lo + i + 64, ... in order (both
-    // values of a tile requested together), then the lanes combined by a fixed butterfly.
-    __syncthreads();                  // every tile's (max, sum) is stored
-    for (int p = w; p < G.n_pairs; p += NW) {
+    // one wave per pair (or the last wave every pair), lane i folding tiles q_lo + i,
+    // q_lo + i + 64, ... in order (both values of a tile requested together), then the
+    // lanes combined by a fixed butterfly.
+    int p_first = w, p_step = NW;
+    if (sDone) {
+        // this wave's tile records are stored; the last wave to count in has them all
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        int v = 0;
+        if (lane == 0)
+            v = atomicAdd(sDone, 1);
+        if (__builtin_amdgcn_readfirstlane(v) != NW - 1)
+            return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        p_first = 0;
+        p_step = 1;
+    } else {
+        __syncthreads();              // every tile's (max, sum) is stored
+    }
+    for (int p = p_first; p < G.n_pairs; p += p_step) {
         const int64_t row = ((int64_t)b * S.total_pairs + G.pair0 + p) * a.n_tiles;
         double Ml = -INFINITY, Sl = 0.0;
         for (int t = q_lo + lane; t < q_hi; t += 64) {
@@ -472,7 +495,8 @@ __global__ __launch_bounds__(64 * kProbWaves)
 __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_pair_kernel(ScoreArgs a)
 {
     __shared__ __align__(16) uint8_t sK[kProbWaves * prob_tile_bytes(D1 > D2 ? D1 : D2)];
-    __shared__ int sNext;
+    __shared__ int sNext[2];
+    __shared__ int sDone;
     __shared__ int sPage[FLAT ? 1 : kPageCache];
     const int x = blockIdx.x;
     const int half = a.prob_ng / 2;
@@ -481,9 +505,23 @@ __attribute__((amdgpu_waves_per_eu(kProbWaves / 4))) void srh_prob_pair_kernel(S
     const int i = x / per;
     const int b = (x - i * per) / G0.parts;
     const int part = x - i * per - b * G0.parts;
-    prob_logits<D1, FLAT>(a, a.grp[a.prob_g0 + i], b, part, sK, sNext, sPage);
-    __syncthreads();                  // the LDS areas and the tile counter are free again
-    prob_logits<D2, FLAT>(a, a.grp[a.prob_g0 + half + i], b, part, sK, sNext, sPage);
+    if constexpr (FLAT) {
+        // a tile counter per group, both zeroed up front, and every wave's LDS area the same
+        // for both head dims: a wave goes from its last tile of the first group straight
+        // to the second, and the last one to finish the first group folds it meanwhile
+        if (threadIdx.x == 0) {
+            sNext[0] = sNext[1] = 0;
+            sDone = 0;
+        }
+        __syncthreads();
+        constexpr int kWave = prob_tile_bytes(D1 > D2 ? D1 : D2);
+        prob_logits<D1, FLAT>(a, a.grp[a.prob_g0 + i], b, part, sK, sNext[0], sPage, false, kWave, &sDone);
+        prob_logits<D2, FLAT>(a, a.grp[a.prob_g0 + half + i], b, part, sK, sNext[1], sPage, false, kWave);
+    } else {
+        prob_logits<D1, FLAT>(a, a.grp[a.prob_g0 + i], b, part, sK, sNext[0], sPage);
+        __syncthreads();              // the LDS areas and the page cache are free again
+        prob_logits<D2, FLAT>(a, a.grp[a.prob_g0 + half + i], b, part, sK, sNext[1], sPage);
+    }
 }
 
 // ---- logit-sum mode: raw scaled logits on MFMA -------------------------------------
