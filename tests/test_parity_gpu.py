@@ -568,6 +568,39 @@ def test_selection_two_workgroups_match_one():
     say("  two-workgroup and one-workgroup selection identical to the oracle")
 
 
+def test_selection_at_64k_positions():
+    """The widest selection variant (64 keys per thread) at its size limit, through the C
+    ABI with and without a workspace, against the oracle: a sequence whose two tiers sum to
+    exactly the 4096-candidate cap (two workgroups), one just above it (one workgroup), a
+    budget above the LDS staging area (the ordered set written without staging), and
+    quantised scores (ties) in the combined candidates."""
+    from sparse_kv_attention_amd import dustin as D
+    B, n_max, k_max = 4, 65536, 17000
+    ctx = np.array([65536, 65536, 65535, 40000], dtype=np.int32)
+    budget = np.array([4368, 4369, 17000, 3000], dtype=np.int32)   # r + m = 4096, 4097, ...
+    sink = np.array([16, 16, 16, 7], dtype=np.int32)
+    window = np.array([256, 256, 512, 100], dtype=np.int32)
+    m = np.array([1500, 1500, 6000, 2000], dtype=np.int32)
+    gen = np.random.default_rng(88)
+    sd = gen.uniform(0, 1e-4, (B, n_max)).astype(np.float32)
+    st = gen.uniform(0, 1e-4, (B, n_max)).astype(np.float32)
+    st[0] = np.round(st[0] * 2e5) / 2e5
+    want_idx, want_cnt = O.select(ctx, sd, st, budget, sink, window, m, k_max)
+    dev = "cuda"
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    ws = D.workspace(D.dustin_select_workspace_size(B, n_max), dev)
+    for name, w in (("two workgroups", ws), ("one workgroup", None)):
+        idx = torch.full((B, k_max), -5, dtype=torch.int32, device=dev)
+        cnt = torch.zeros((B,), dtype=torch.int32, device=dev)
+        D.dustin_select(t(ctx), t(sd), t(st), t(budget), t(sink), t(window), t(m), idx, cnt, w)
+        torch.cuda.synchronize()
+        assert np.array_equal(cnt.cpu().numpy(), want_cnt), name
+        got = idx.cpu().numpy()
+        for b in range(B):
+            assert np.array_equal(got[b], want_idx[b]), f"{name}: sequence {b}"
+    say("  64k-position selection identical to the oracle on both paths")
+
+
 def test_context_above_32k():
     """Contexts of 30k..50k tokens (ragged): 64 keys per selection thread (the widest
     selection variant), scoring over 50k-token rows, a 4096-token budget over two splits
