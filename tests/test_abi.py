@@ -170,6 +170,7 @@ def test_workspace_queries():
     n.value = 7
     assert D._dense_ws(0, 64, 8, 128, 5, 32768, ctypes.byref(n)) == D.OK and n.value == 0
     assert D._select_ws(8, 32768, ctypes.byref(n)) == D.OK
+    assert n.value == 8 * (2 * 1024 + 1) * 8    # two tiers' position masks + a counter per sequence
     assert D._score_ws(8, 32768, 4, 5, D.SCORE_PROB_SUM, ctypes.byref(n)) == D.OK
     assert n.value >= 8 * 20 * 32768 * 4
     assert D._score_ws(8, 32768, 4, 5, D.SCORE_LOGIT_SUM_ALL, ctypes.byref(n)) == D.OK
@@ -220,7 +221,11 @@ def test_score_rejects():
 
 def test_select_rejects():
     f = lambda **kw: D._select(2, kw.get("n_max", 4096), FAKE, kw.get("sd", FAKE), kw.get("st", FAKE), FAKE, FAKE,
-                               FAKE, FAKE, kw.get("k_max", 256), kw.get("idx", FAKE), FAKE, None, 0, None)
+                               FAKE, FAKE, kw.get("k_max", 256), kw.get("idx", FAKE), FAKE, kw.get("ws", None),
+                               kw.get("wsb", 0), None)
+    need = 2 * (2 * 1024 + 1) * 8
+    assert f(ws=FAKE, wsb=need - 1) == D.ERR_WORKSPACE   # a workspace, but short of the query
+    assert f(ws=FAKE + 8, wsb=need) == D.ERR_WORKSPACE   # not 16-byte aligned
     assert f(st=FAKE + 4) == D.ERR_INVALID_ARG        # scores are read as 16-byte vectors
     assert f(sd=FAKE + 8) == D.ERR_INVALID_ARG
     assert f(n_max=65537) == D.ERR_UNSUPPORTED
