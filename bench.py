@@ -270,6 +270,20 @@ def main():
             D.dustin_sparse_verify_attn(q1[l], k, v, T.hkv, inp.ctx_len, step.idx, step.count, step.scale,
                                         o1, l1, ws1)
     us_decode = timed(decode_all, reps) / len(attn_layers)
+    # the gather floor of the same lists: the attention's K and V list rows read the same
+    # way with every row in flight and no arithmetic, 80 layers back to back (unpaged views)
+    us_floor = None
+    if not any(step.kv[l][0].page_table or step.kv[l][1].page_table for l in attn_layers):
+        fl_idx = step.idx[:, :inp.k_max].contiguous()
+        fl_ck = torch.zeros((B, T.hkv), dtype=torch.int32, device=dev)
+
+        def floor_all():
+            for l in attn_layers:
+                k, v = step.kv[l]
+                D.dustin_gather_floor(k, v, T.hkv, T.d, fl_idx, fl_ck)
+        floor_all()
+        us_floor = timed(floor_all, reps) / len(attn_layers)
+    b_floor = B * T.hkv * inp.k_max * 2 * T.d * 2
     b_decode = attn_bytes(B, T.hq, T.hkv, T.d, 1, counts)
     rec_layers = [l for l in (attn_layers[0], 60) if l in step.kv]
     recovery = {}
@@ -366,6 +380,12 @@ def main():
                      "kernel": "dustin_sparse_verify_attn, one layer: " + D.attn_kernel_names(T.d, plan),
                      "plan": plan, "algorithmic_bytes_per_call": b_attn, "call_us": round(us_attn_call, 2)},
     }
+    if us_floor is not None:
+        # the same list rows gathered with no arithmetic (dustin_gather_floor): the ceiling
+        # for these bytes as laid out, and the call's time over it
+        line["roofline"]["gather_floor"] = {"us": round(us_floor, 2), "bytes": b_floor,
+                                            "gbs": round(b_floor / (us_floor * 1e-6) / 1e9, 1),
+                                            "call_over_floor": round(us_attn_call / us_floor, 3)}
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp, step, args.cpu_seconds, b_attn, b_score, b_select, attn_layers)

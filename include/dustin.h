@@ -287,6 +287,27 @@ dustin_status dustin_sparse_verify_attn_noalloc(int B, int Hq, int Hkv, int head
                                                 const int32_t *count, int k_max, float scale,
                                                 void *out, float *lse, void *stream);
 
+/* dustin_gather_floor — a measurement call for tools that rate the verification
+ * attention against its memory ceiling (the English Dustin summary's "Problem Statement":
+ * memory access sets the latency): it reads exactly the K and V row slices of the list
+ * entries that dustin_sparse_verify_attn reads for them, and computes nothing.  For every
+ * sequence b, KV head g and list entry j < k_max it reads the head_dim bf16 elements of
+ * K[b][i][g] and V[b][i][g], i = idx[b][j] clamped to [0, min(k->n_tokens, v->n_tokens)),
+ * with 16-byte non-temporal loads and every row of a workgroup's 512 entries in flight at
+ * once.  Its time per launch is the gather floor for those bytes as they lie in memory.
+ *   idx      : int32 [B][k_max] (device); every entry is read, whatever the list count
+ *   k, v     : contiguous (unpaged) views; paged -> DUSTIN_ERR_UNSUPPORTED
+ *   head_dim : 64 or 128
+ *   checksum : uint32 [B][Hkv] (device, 4-byte aligned).  mode 1: XOR of every 32-bit
+ *              word read for (b, g) is XOR-ed into checksum[b][g] (zero it first to get
+ *              the XOR itself).  mode 0 (timing): left unchanged, except that a
+ *              workgroup lane whose own XOR equals 0x9e3779b9 stores it there (the store
+ *              keeps the loads; with real data it practically never happens).
+ * B == 0 or k_max == 0 enqueues nothing. */
+dustin_status dustin_gather_floor(int B, int Hkv, int head_dim, const dustin_kv_view *k /* host */,
+                                  const dustin_kv_view *v /* host */, const int32_t *idx, int k_max,
+                                  uint32_t *checksum, int mode, void *stream);
+
 dustin_status dense_verify_attn_workspace_size(int B, int Hq, int Hkv, int head_dim,
                                                int n_verify, int n_max,
                                                size_t *bytes /* host */);

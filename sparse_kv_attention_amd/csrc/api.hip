@@ -7,6 +7,7 @@
 #include <mutex>
 
 #include "dustin.h"
+#include "floor.hpp"
 #include "kv.hpp"
 #include "launch.hpp"
 
@@ -647,6 +648,45 @@ dustin_status dustin_attn_plan(int B, int Hq, int Hkv, int head_dim, int n_verif
     plan[3] = (int32_t)lay.plan.grid;
     plan[4] = lay.plan.splits == 1 ? 0 : (env_flag("DUSTIN_ATTN_FUSED_MERGE", false) ? 2 : 1);
     return DUSTIN_OK;
+}
+
+dustin_status dustin_gather_floor(int B, int Hkv, int head_dim, const dustin_kv_view *k, const dustin_kv_view *v,
+                                  const int32_t *idx, int k_max, uint32_t *checksum, int mode, void *stream)
+{
+    if (B < 0 || Hkv <= 0 || k_max < 0 || (mode != 0 && mode != 1))
+        return DUSTIN_ERR_INVALID_ARG;
+    if (head_dim != 64 && head_dim != 128)
+        return DUSTIN_ERR_UNSUPPORTED;
+    if (B == 0 || k_max == 0)
+        return DUSTIN_OK;
+    if (!idx || !checksum || ((uintptr_t)checksum & 3))
+        return DUSTIN_ERR_INVALID_ARG;
+    if (!view_ok(k, Hkv, 1) || !view_ok(v, Hkv, 1))
+        return DUSTIN_ERR_INVALID_ARG;
+    if (k->page_table || v->page_table)
+        return DUSTIN_ERR_UNSUPPORTED;
+    const int splits = (k_max + kFloorPositions - 1) / kFloorPositions;
+    if ((int64_t)B * splits * Hkv > 0x7fffffff)
+        return DUSTIN_ERR_UNSUPPORTED;
+    FloorArgs a;
+    a.B = B;
+    a.Hkv = Hkv;
+    a.k_max = k_max;
+    a.n_tok = std::min(k->n_tokens, v->n_tokens);
+    a.splits = splits;
+    a.k = static_cast<const uint16_t *>(k->base);
+    a.v = static_cast<const uint16_t *>(v->base);
+    a.k_sb = k->stride_batch;
+    a.k_st = k->stride_token;
+    a.k_sh = k->stride_head;
+    a.v_sb = v->stride_batch;
+    a.v_st = v->stride_token;
+    a.v_sh = v->stride_head;
+    a.idx = idx;
+    a.checksum = checksum;
+    a.mode = mode;
+    const hipError_t e = launch_gather_floor(a, head_dim, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DUSTIN_OK : DUSTIN_ERR_HIP;
 }
 
 dustin_status dustin_kv_write_block(int B, int Hkv, int head_dim, int n_new, const void *k_new,

@@ -92,6 +92,8 @@ _kv_write = _decl("dustin_kv_write_block", [_I, _I, _I, _I, _P, _P, _P, ctypes.P
                                              ctypes.POINTER(KvView), _P])
 _kv_commit = _decl("dustin_kv_commit", [_I, _I, _P, _P, _P])
 _recovery = _decl("dustin_attn_recovery", [_I, _P, _P, _P, _P])
+_floor = _decl("dustin_gather_floor", [_I, _I, _I, ctypes.POINTER(KvView), ctypes.POINTER(KvView), _P, _I, _P,
+                                       _I, _P])
 
 EXPORTED = ("dustin_status_string", "dustin_srh_score_workspace_size", "dustin_srh_score",
             "dustin_srh_score_signals_workspace_size", "dustin_srh_score_signals",
@@ -99,7 +101,7 @@ EXPORTED = ("dustin_status_string", "dustin_srh_score_workspace_size", "dustin_s
             "dustin_sparse_verify_attn_workspace_size", "dustin_sparse_verify_attn",
             "dustin_sparse_verify_attn_noalloc", "dustin_attn_plan", "dustin_sparse_verify_attn_logits",
             "dense_verify_attn_workspace_size", "dense_verify_attn",
-            "dustin_kv_write_block", "dustin_kv_commit", "dustin_attn_recovery")
+            "dustin_kv_write_block", "dustin_kv_commit", "dustin_attn_recovery", "dustin_gather_floor")
 
 
 class DustinError(RuntimeError):
@@ -381,6 +383,18 @@ def dustin_attn_recovery(lse_sparse, lse_dense, rec, stream=None):
         raise ValueError("lse_sparse, lse_dense and rec must have the same shape")
     _check(_recovery(rec.numel(), _ptr(lse_sparse), _ptr(lse_dense), _ptr(rec), _stream(stream)),
            "dustin_attn_recovery")
+
+
+def dustin_gather_floor(k: KvView, v: KvView, Hkv: int, head_dim: int, idx, checksum, mode: int = 0,
+                        stream=None):
+    """Reads the K and V rows of idx [B][k_max] (int32) the way the sparse attention does
+    and computes nothing; checksum: uint32 [B][Hkv] (as int32) receives the XOR of the words
+    read in mode 1."""
+    _dev_i32(idx, "idx"); _dev_i32(checksum, "checksum")
+    if idx.dim() != 2 or tuple(checksum.shape) != (idx.shape[0], Hkv):
+        raise ValueError("idx must be [B][k_max] and checksum [B][Hkv]")
+    _check(_floor(idx.shape[0], Hkv, head_dim, ctypes.byref(k), ctypes.byref(v), _ptr(idx), idx.shape[1],
+                  _ptr(checksum), int(mode), _stream(stream)), "dustin_gather_floor")
 
 
 def raw_library():

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     assert set(names) == set(D.EXPORTED)
     out = subprocess.run(["nm", "-D", "--defined-only", D.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
@@ -252,6 +252,27 @@ def test_kv_write_block_rejects():
     assert f(kv=small) == D.ERR_INVALID_ARG          # the block does not fit the view
     assert f(vv=view(n_heads=4)) == D.ERR_INVALID_ARG
     assert f(B=0, kn=None, vn=None, ctx=None) == D.OK
+
+
+def test_gather_floor_rejects():
+    k = view()
+
+    def f(B=2, Hkv=8, d=128, kv=k, vv=k, idx=FAKE, k_max=2048, ck=FAKE, mode=0):
+        return D._floor(B, Hkv, d, ctypes.byref(kv), ctypes.byref(vv), idx, k_max, ck, mode, None)
+
+    assert f(d=96) == D.ERR_UNSUPPORTED
+    assert f(mode=2) == D.ERR_INVALID_ARG
+    assert f(Hkv=0) == D.ERR_INVALID_ARG
+    assert f(B=-1) == D.ERR_INVALID_ARG
+    assert f(k_max=-1) == D.ERR_INVALID_ARG
+    assert f(idx=None) == D.ERR_INVALID_ARG
+    assert f(ck=None) == D.ERR_INVALID_ARG
+    assert f(ck=FAKE + 2) == D.ERR_INVALID_ARG
+    assert f(vv=view(n_heads=4)) == D.ERR_INVALID_ARG
+    assert f(kv=view(page_table=FAKE, page_size=16, max_pages=8, num_pages=8, stride_page=16 * 1024)) \
+        == D.ERR_UNSUPPORTED
+    assert f(B=0, idx=None, ck=None) == D.OK
+    assert f(k_max=0, idx=None, ck=None) == D.OK
 
 
 def test_kv_commit_and_recovery_reject():

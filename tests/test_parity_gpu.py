@@ -698,3 +698,39 @@ def test_single_query_signals():
     check_pipeline(W.make_inputs(w, device="cuda"), [0], [], [0, 1])
     w = small("collect2_nq1", 2, 900, 8, 2, 128, 0, 120, 0, 0, 0, seed=30)
     check_pipeline(W.make_inputs(w, device="cuda"), [0], [], [0, 1], logit_sum2=True)
+
+
+def floor_xor(kc: torch.Tensor, vc: torch.Tensor, idx: np.ndarray) -> np.ndarray:
+    """[B][Hkv] XOR of every 32-bit word of the K and V rows of idx (clamped to the cache):
+    what dustin_gather_floor's checksum mode computes, from its definition."""
+    n = kc.shape[1]
+    k32 = kc.contiguous().view(torch.int16).numpy().view(np.uint32)
+    v32 = vc.contiguous().view(torch.int16).numpy().view(np.uint32)
+    tok = np.clip(idx, 0, n - 1)
+    out = np.zeros((kc.shape[0], kc.shape[2]), dtype=np.uint32)
+    for b in range(kc.shape[0]):
+        out[b] = (np.bitwise_xor.reduce(k32[b, tok[b]], axis=(0, 2))
+                  ^ np.bitwise_xor.reduce(v32[b, tok[b]], axis=(0, 2)))
+    return out
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_gather_floor_reads_the_list_rows(d):
+    """The gather-floor call reads exactly the list rows: its XOR checksum over a ragged
+    list (three workgroups of 512, 512 and 276 entries) with out-of-range entries (clamped)
+    matches the XOR of those rows on the host; the timing mode leaves the checksum alone."""
+    from sparse_kv_attention_amd import dustin as D
+    g = torch.Generator().manual_seed(41 + d)
+    B, N, Hkv, k_max = 3, 2500, 3, 1300
+    kc = torch.randn((B, N, Hkv, d), generator=g).to(torch.bfloat16)
+    vc = torch.randn((B, N, Hkv, d), generator=g).to(torch.bfloat16)
+    idx = torch.randint(-40, N + 40, (B, k_max), generator=g, dtype=torch.int32)
+    kd, vd, idd = kc.cuda(), vc.cuda(), idx.cuda()
+    ck = torch.zeros((B, Hkv), dtype=torch.int32, device="cuda")
+    D.dustin_gather_floor(D.kv_view(kd), D.kv_view(vd), Hkv, d, idd, ck, mode=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(ck.cpu().numpy().view(np.uint32), floor_xor(kc, vc, idx.numpy()))
+    ck0 = torch.full((B, Hkv), 7, dtype=torch.int32, device="cuda")
+    D.dustin_gather_floor(D.kv_view(kd), D.kv_view(vd), Hkv, d, idd, ck0, mode=0)
+    torch.cuda.synchronize()
+    assert bool((ck0 == 7).all())

@@ -10,7 +10,7 @@ import torch
 
 from _harness import say
 from sparse_kv_attention_amd import workloads as W
-from test_parity_gpu import check_pipeline
+from test_parity_gpu import check_pipeline, floor_xor
 
 pytestmark = pytest.mark.gpu
 
@@ -24,6 +24,15 @@ def test_qwen72b_b8_n32768_sampled():
         hit = np.isin(inp.needles[b].numpy(), sel[b]).mean()
         say(f"  needles kept in sequence {b}: {hit:.3f}")
         assert hit > 0.9
+    # the gather floor the bench times reads exactly layer 0's rows of the selected lists
+    from sparse_kv_attention_amd import dustin as D
+    T = inp.w.target
+    idx = step.idx[:, :inp.k_max].contiguous()
+    ck = torch.zeros((inp.w.batch, T.hkv), dtype=torch.int32, device="cuda")
+    D.dustin_gather_floor(D.kv_view(inp.k_cache[0]), D.kv_view(inp.v_cache[0]), T.hkv, T.d, idx, ck, mode=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(ck.cpu().numpy().view(np.uint32),
+                          floor_xor(inp.k_cache[0].cpu(), inp.v_cache[0].cpu(), idx.cpu().numpy()))
     del step, inp
     torch.cuda.empty_cache()
 
