@@ -294,7 +294,9 @@ dustin_status dustin_sparse_verify_attn_noalloc(int B, int Hq, int Hkv, int head
  * sequence b, KV head g and list entry j < k_max it reads the head_dim bf16 elements of
  * K[b][i][g] and V[b][i][g], i = idx[b][j] clamped to [0, min(k->n_tokens, v->n_tokens)),
  * with 16-byte non-temporal loads and every row of a workgroup's 512 entries in flight at
- * once.  Its time per launch is the gather floor for those bytes as they lie in memory.
+ * once (when k_max is not a multiple of 512, the last workgroup's lanes past k_max re-read
+ * entry k_max - 1's rows, which the cache serves, and leave them out of the checksum).
+ * Its time per launch is the gather floor for those bytes as they lie in memory.
  *   idx      : int32 [B][k_max] (device); every entry is read, whatever the list count
  *   k, v     : contiguous (unpaged) views; paged -> DUSTIN_ERR_UNSUPPORTED
  *   head_dim : 64 or 128
