@@ -131,7 +131,7 @@ def main():
 
     if args.counters:
         # a plain copy of CALIB_BYTES (read CALIB_BYTES, write CALIB_BYTES), then ten
-        # distinct-layer attention calls
+        # distinct-layer attention calls and the gather floor on the same ten layers
         src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev).random_(0, 255)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -140,6 +140,12 @@ def main():
         step.select()
         for l in step.layers[:10]:
             step.attn(l)
+        from sparse_kv_attention_amd import dustin as D
+        fl_idx = step.idx[:, :inp.k_max].contiguous()
+        fl_ck = torch.zeros((B, T.hkv), dtype=torch.int32, device=dev)
+        for l in step.layers[:10]:
+            k, v = step.kv[l]
+            D.dustin_gather_floor(k, v, T.hkv, T.d, fl_idx, fl_ck)
         torch.cuda.synchronize()
         print(json.dumps({"counters_run": True, "calib_bytes": CALIB_BYTES, "attn_calls": 10,
                           "attn_source_sha256_16": attn_source_hash()}), flush=True)
